@@ -1,0 +1,207 @@
+"""Exact scaled-dot-product attention on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of libfa.so (include/fa.h). Every step of
+the computation runs in the library's HIP kernels; this module only checks
+tensors, allocates outputs with torch on the GPU and passes raw pointers and
+the current HIP stream. There is no CPU fallback: without the built library
+or without a GPU the calls raise.
+
+The C functions are re-exported under their own names (fa_fwd, fa_bwd,
+fa_bwd_workspace_bytes, fa_status_str, fa_abi_version), taking plain ints
+for pointers. The tensor-level helpers are forward(), backward() and the
+autograd wrapper FlashAttention / attention().
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # imported before libfa.so so the process shares torch's HIP runtime
+
+__all__ = [
+    "FA_BF16", "FA_F32", "FAError", "library_path", "load_library",
+    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version",
+    "forward", "backward", "FlashAttention", "attention",
+]
+
+FA_BF16 = 0
+FA_F32 = 1
+
+_STATUS = {0: "FA_OK", 1: "FA_E_NULLPTR", 2: "FA_E_SHAPE", 3: "FA_E_DTYPE", 4: "FA_E_HEADDIM",
+           5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({fa_status_str(status)})")
+
+
+def library_path() -> str:
+    return os.environ.get("FA_LIBRARY", os.path.join(_HERE, "libfa.so"))
+
+
+def load_library():
+    """Load libfa.so (built in-tree by exact_tiled_attention_29_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_tiled_attention_29_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                           i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_status_str.argtypes = [i32]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i32
+    if lib.fa_abi_version() != 1:
+        raise RuntimeError("libfa.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+# ---- C functions under their own names (pointers as ints) ----
+
+def fa_fwd(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype, causal, scale, stream):
+    return load_library().fa_fwd(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype,
+                                 int(causal), float(scale), stream)
+
+
+def fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype, causal,
+           scale, workspace, workspace_bytes, stream):
+    return load_library().fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q,
+                                 n_k, d, dtype, int(causal), float(scale), workspace,
+                                 workspace_bytes, stream)
+
+
+def fa_bwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, causal):
+    return load_library().fa_bwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, int(causal))
+
+
+def fa_status_str(status: int) -> str:
+    try:
+        return load_library().fa_status_str(status).decode()
+    except RuntimeError:
+        return _STATUS.get(status, "unknown")
+
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+# ---- tensor-level helpers ----
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return FA_BF16
+    if dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {dtype}; expected bfloat16 or float32")
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (the HIP kernels are the only implementation)")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None):
+    """O, L = attention(q, k, v). q: [B,H,n_q,d]; k, v: [B,H,n_k,d].
+
+    o_dtype defaults to the input dtype; torch.float32 gives the unrounded
+    fp32 O for bf16 inputs. Returns (O, L) with L fp32 [B,H,n_q].
+    """
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    dt = _code(q.dtype)
+    _check(q, "q", (B, H, n_q, d))
+    _check(k, "k", (B, H, n_k, d), q.dtype)
+    _check(v, "v", (B, H, n_k, d), q.dtype)
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=o_dtype, device=q.device)
+    _check(out, "out", (B, H, n_q, d), o_dtype)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    _check(lse, "lse", (B, H, n_q), torch.float32)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _code(o_dtype),
+                lse.data_ptr(), B, H, n_q, n_k, d, dt, causal, scale, _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grads=None):
+    """dQ, dK, dV from the forward's O and L and the upstream gradient dO."""
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    dt = _code(q.dtype)
+    _check(q, "q", (B, H, n_q, d))
+    _check(k, "k", (B, H, n_k, d), q.dtype)
+    _check(v, "v", (B, H, n_k, d), q.dtype)
+    _check(o, "o", (B, H, n_q, d))
+    _check(lse, "lse", (B, H, n_q), torch.float32)
+    _check(do, "do", (B, H, n_q, d), q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_bwd_workspace_bytes(B, H, n_q, n_k, d, dt, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _code(o.dtype),
+                lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                B, H, n_q, n_k, d, dt, causal, scale, workspace.data_ptr(), workspace.numel(),
+                _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+class FlashAttention(torch.autograd.Function):
+    """autograd wrapper: the forward saves only Q, K, V, O and L; the
+    backward rebuilds P from L inside the kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal=False, scale=None):
+        o, lse = forward(q, k, v, causal, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal = causal
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal=False, scale=None):
+    return FlashAttention.apply(q, k, v, causal, scale)

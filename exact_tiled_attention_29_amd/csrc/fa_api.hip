@@ -1,0 +1,141 @@
+// C-ABI entry points of libfa.so: argument checks on the host (before any
+// HIP call), workspace sizing and dispatch to the kernel launchers.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dim_ok(int d, int dtype) {
+    if (dtype == FA_BF16) return d == 64 || d == 128;
+    if (dtype == FA_F32) return d == 16 || d == 32 || d == 64 || d == 128;
+    return false;
+}
+
+// Shared checks of the forward and backward calls. Sets *empty when there
+// is nothing to compute for the query side (batch, heads or n_q is zero).
+int check_common(int batch, int heads, int n_q, int n_k, int d, int dtype, int o_dtype,
+                 float scale, bool* empty) {
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_DTYPE;
+    if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_E_DTYPE;
+    if (dtype == FA_F32 && o_dtype != FA_F32) return FA_E_DTYPE;
+    if (batch < 0 || heads < 0 || n_q < 0 || n_k < 0) return FA_E_SHAPE;
+    if (!dim_ok(d, dtype)) return FA_E_HEADDIM;
+    if (!(isfinite(scale) && scale > 0.0f)) return FA_E_SCALE;
+    const long long bh = (long long)batch * heads;
+    if (bh > 0x7fffffffLL) return FA_E_SHAPE;
+    // Every element offset must fit in 63 bits and the per-row grids in 31.
+    const long long rows = bh * (long long)(n_q > n_k ? n_q : n_k);
+    if (rows > (1LL << 40)) return FA_E_SHAPE;
+    *empty = bh == 0 || n_q == 0;
+    if (!(*empty) && n_k == 0) return FA_E_SHAPE;
+    return FA_OK;
+}
+
+size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
+    const size_t rows = (size_t)bh * (size_t)n_q;
+    size_t b = align_up(rows * sizeof(float));                     // D
+    if (dtype == FA_BF16) b += align_up(rows * (size_t)d * sizeof(float));  // dQ accumulator
+    return b;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return 1; }
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_E_NULLPTR: return "null pointer argument";
+        case FA_E_SHAPE: return "invalid shape";
+        case FA_E_DTYPE: return "unsupported dtype";
+        case FA_E_HEADDIM: return "unsupported head dimension";
+        case FA_E_SCALE: return "scale must be finite and > 0";
+        case FA_E_WORKSPACE: return "workspace missing or too small";
+        case FA_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+           int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+           void* stream) {
+    bool empty = false;
+    int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, scale, &empty);
+    if (st != FA_OK) return st;
+    if (empty) return FA_OK;
+    if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
+    fa::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.bh = batch * heads; a.n_q = n_q; a.n_k = n_k; a.d = d;
+    a.causal = causal != 0; a.o_f32 = o_dtype == FA_F32; a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int dtype, int causal) {
+    (void)causal;
+    bool empty = false;
+    const int o_dtype = dtype == FA_F32 ? FA_F32 : FA_BF16;
+    if (check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, 1.0f, &empty) != FA_OK) return 0;
+    if (empty) return 0;
+    return workspace_bytes((long long)batch * heads, n_q, d, dtype);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+           const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+           int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+           void* workspace, size_t workspace_bytes_given, void* stream) {
+    bool empty = false;
+    int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, scale, &empty);
+    if (st != FA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const long long bh = (long long)batch * heads;
+    if (empty) {
+        // No query rows: the gradient of K and V is zero.
+        if (bh == 0 || n_k == 0) return FA_OK;
+        if (!dk || !dv) return FA_E_NULLPTR;
+        const size_t bytes = (size_t)bh * n_k * d * (dtype == FA_BF16 ? 2 : 4);
+        hipError_t e = fa::launch_zero(dk, bytes, s);
+        if (e == hipSuccess) e = fa::launch_zero(dv, bytes, s);
+        return hip_status(e);
+    }
+    if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return FA_E_NULLPTR;
+    const size_t need = workspace_bytes(bh, n_q, d, dtype);
+    if (!workspace || workspace_bytes_given < need) return FA_E_WORKSPACE;
+    if (((uintptr_t)workspace) % kAlign != 0) return FA_E_WORKSPACE;
+    fa::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.d_o = d_o;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.bh = (int)bh; a.n_q = n_q; a.n_k = n_k; a.d = d;
+    a.causal = causal != 0; a.o_f32 = o_dtype == FA_F32; a.scale = scale;
+    char* w = (char*)workspace;
+    a.drow = (float*)w;
+    a.dq_acc = dtype == FA_BF16 ? (float*)(w + align_up((size_t)bh * n_q * sizeof(float))) : nullptr;
+    return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
+}
+
+}  // extern "C"
+
+namespace fa {
+
+int fwd_bf16_qb_override() {
+    static const int v = [] {
+        const char* e = getenv("FA_FWD_QB");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
+}  // namespace fa

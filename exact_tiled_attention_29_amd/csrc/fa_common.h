@@ -1,0 +1,85 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// D(32x32, fp32) += A(32x16) * B(16x32), bf16 operands.
+// A: lane l holds row (l % 32), 8 consecutive k-slots of half (l / 32).
+// B: lane l holds column (l % 32), the same 8 k-slots as A.
+// D: lane l holds column (l % 32); element v is row 8*(v/4) + 4*(l/32) + v%4.
+// Only the row/column placement matters to the callers: a contraction sums
+// over all k-slots, so any bijection of keys onto slots works as long as A
+// and B use the same one.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator held in element v by lane-half g.
+__device__ __forceinline__ constexpr int acc_row(int v, int g) {
+    return 8 * (v >> 2) + 4 * g + (v & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Combine a value with the one held by the lane 32 positions away
+// (l <-> l ^ 32). v_permlane32_swap with the same register as both operands
+// leaves, in every lane, its own value in one result and its partner's in
+// the other, so max / sum of the two results is the pairwise reduction
+// whichever half each lands in.
+__device__ __forceinline__ float halves_max(float x) {
+    unsigned u = __builtin_bit_cast(unsigned, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+    unsigned u = __builtin_bit_cast(unsigned, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// fp32 -> bf16, round to nearest even (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    bf16x8 z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+    return z;
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+// Map a hardware workgroup index to a logical one so that each of the 8
+// XCDs (which receive workgroups round-robin: id % 8) works through one
+// contiguous range of logical ids. Bijective for any n.
+__device__ __forceinline__ int xcd_logical_id(int bid, int n) {
+    const int q = n >> 3, rem = n & 7;
+    const int xcd = bid & 7, slot = bid >> 3;
+    return xcd < rem ? xcd * (q + 1) + slot : rem * (q + 1) + (xcd - rem) * q + slot;
+}
+
+}  // namespace fa

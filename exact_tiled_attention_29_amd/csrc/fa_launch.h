@@ -1,0 +1,59 @@
+// Host-side launchers of the attention kernels (internal to libfa.so).
+// Arguments are validated by the C-ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int bh;  // batch * heads
+    int n_q, n_k, d;
+    bool causal;
+    bool o_f32;  // O stored as float32 (else bf16)
+    float scale;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* d_o;
+    void* dq;
+    void* dk;
+    void* dv;
+    int bh;
+    int n_q, n_k, d;
+    bool causal;
+    bool o_f32;
+    float scale;
+    float* dq_acc;  // fp32 [bh, n_q, d] (bf16 path only)
+    float* drow;    // fp32 [bh, n_q]: D = rowsum(dO * O)
+};
+
+// bf16 path (MFMA).
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
+int fwd_bf16_rows_per_wg(const FwdArgs& a);
+
+// float32 path (fp32 FMA).
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st);
+
+// Zero `bytes` bytes (a multiple of 4) with a fill kernel; no memset node,
+// so the call is safe under stream capture.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+// Tuning override read once from the environment (FA_FWD_QB = 1 or 2);
+// 0 when unset. Used by the sweep in the bench harness.
+int fwd_bf16_qb_override();
+
+}  // namespace fa

@@ -1,0 +1,121 @@
+/*
+ * fa.h - exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfa.so. Every tensor argument is a HIP device pointer to a
+ * contiguous row-major array; sizes are plain ints; the stream is a
+ * hipStream_t passed as void* (NULL = the default stream). No call allocates
+ * or frees device memory and the library keeps no global state, so calls on
+ * different streams may run concurrently.
+ *
+ * Layout: Q, O, dO, dQ are [batch, heads, n_q, d]; K, V, dK, dV are
+ * [batch, heads, n_k, d]; L is [batch, heads, n_q]. Offsets are 64-bit.
+ *
+ * Errors: every argument is checked on the host before any HIP call. On a
+ * failed check nothing is launched, no output is touched and a status code
+ * is returned. A failed launch returns FA_E_HIP. Calls are asynchronous: a
+ * fault inside a kernel surfaces at the caller's next synchronisation.
+ *
+ * Supported: dtype FA_BF16 with d in {64, 128}; dtype FA_F32 with d in
+ * {16, 32, 64, 128}. n_k >= 1 whenever there is work (a softmax over zero
+ * keys is undefined). batch, heads or n_q equal to 0 is an empty call: the
+ * forward does nothing; the backward zeroes dK and dV when n_q == 0.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_BF16 = 0, /* bfloat16 storage; products on bf16 MFMA, accumulation in fp32 */
+    FA_F32 = 1   /* float32 storage and arithmetic */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_E_NULLPTR = 1,   /* a required pointer is NULL                         */
+    FA_E_SHAPE = 2,     /* negative size, n_k == 0 with work to do, or too big */
+    FA_E_DTYPE = 3,     /* unknown dtype / o_dtype, or an unsupported pairing  */
+    FA_E_HEADDIM = 4,   /* d not supported for this dtype                      */
+    FA_E_SCALE = 5,     /* scale not finite or not > 0                         */
+    FA_E_WORKSPACE = 6, /* backward workspace NULL or smaller than required    */
+    FA_E_HIP = 7        /* a HIP launch or runtime call failed                 */
+} fa_status;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [+ causal mask]) V and
+ * L = logsumexp of each masked, scaled score row (natural log), without
+ * ever forming the n_q x n_k score matrix in memory.
+ *
+ * Defined by: the attention formula on page 2 ("FlashAttention：深度学习中的
+ * 高效注意力机制", section 公式推导); the tiled forward with running max m and
+ * running sum l, O rescaled by exp(m_old - m_new) per key tile, and the
+ * outputs O / l and L = m + log(l), on page 1 ("05_flash_attention.py",
+ * section 2, flash_attention_forward).
+ *
+ * q      [B,H,n_q,d] dtype       k, v  [B,H,n_k,d] dtype
+ * o      [B,H,n_q,d] o_dtype     (o_dtype: FA_BF16 or FA_F32; FA_F32 inputs
+ *                                 require FA_F32 output). A bf16 O is the
+ *                                 round-to-nearest-even rounding of the fp32
+ *                                 result.
+ * lse    [B,H,n_q] float32, natural-log logsumexp L.
+ * causal 0: every key visible. 1: key j visible to query i iff j <= i
+ *        (top-left aligned, also when n_q != n_k: page 1, section 2,
+ *        standard_attention masks the strict upper triangle).
+ * scale  multiplies Q K^T; the usual value is 1/sqrt(d). Finite, > 0.
+ * Outputs are written for every row < n_q and nothing else is written.
+ */
+int fa_fwd(const void* q, const void* k, const void* v,
+           void* o, int o_dtype, float* lse,
+           int batch, int heads, int n_q, int n_k, int d, int dtype,
+           int causal, float scale, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (0 for an empty
+ * call). bf16: an fp32 dQ accumulator [B,H,n_q,d] plus the fp32 row term
+ * D [B,H,n_q]; float32: D only. Returns 0 for arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
+                              int dtype, int causal);
+
+/*
+ * Backward pass by recomputation: from Q, K, V, the forward's O and L and the
+ * upstream gradient dO, computes dQ, dK, dV. P is rebuilt tile by tile as
+ * exp(scale * Q K^T - L); D = rowsum(dO * O); dV = P^T dO; dP = dO V^T;
+ * dS = P * (dP - D); dQ = scale * dS K; dK = scale * dS^T Q.
+ *
+ * Defined by: page 1 ("05_flash_attention.py", section 3,
+ * flash_attention_backward and its docstring: the two tricks of rebuilding
+ * P from the saved logsumexp and of D = rowsum(dO * O)); page 3 ("Flash
+ * Attention", section 1.5, the derivatives of O = PV and of P = softmax(S)).
+ *
+ * o, lse are the outputs of fa_fwd for the same q, k, v, causal and scale
+ * (o in o_dtype). d_o [B,H,n_q,d] dtype. dq [B,H,n_q,d], dk, dv [B,H,n_k,d]
+ * in dtype; every element is overwritten.
+ * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller, contents on entry ignored. Calls
+ * that overlap in time must not share a workspace.
+ * bf16 dQ is accumulated with fp32 atomics, so its last bits may vary from
+ * run to run; dK, dV and the float32 path are deterministic.
+ */
+int fa_bwd(const void* q, const void* k, const void* v,
+           const void* o, int o_dtype, const float* lse, const void* d_o,
+           void* dq, void* dk, void* dv,
+           int batch, int heads, int n_q, int n_k, int d, int dtype,
+           int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/* ABI version of this header: 1. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,103 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the
+binding and compare with the fp64 oracle on the same seeded inputs.
+
+Tolerances (max absolute error against the fp64 oracle):
+  bf16 inputs: O (the kernel's unrounded fp32 output) <= 1e-2, L <= 1e-3,
+               each gradient <= 2e-2 * max|reference gradient|; the bf16 O
+               must equal the round-to-nearest-even rounding of the fp32 O.
+  fp32 inputs: O, L <= 1e-5, each gradient <= 1e-5 * max|reference|.
+When an exact gradient is identically zero (a single key: every softmax row
+is the constant 1, so dQ = dK = 0), "max|reference|" is floored at 1e-3 of
+the largest reference gradient of the three, so the bar stays relative to
+the gradients' scale instead of collapsing to 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import exact_tiled_attention_29_amd as fa
+import oracle
+
+TOL = {
+    "bf16": {"O": 1e-2, "L": 1e-3, "grad": 2e-2},
+    "f32": {"O": 1e-5, "L": 1e-5, "grad": 1e-5},
+}
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def to_gpu(*ts):
+    return [t.to("cuda").contiguous() for t in ts]
+
+
+def run(q, k, v, do, causal, scale=None, backward=True):
+    """Run the HIP forward (fp32 O and input-dtype O) and, optionally, the
+    backward fed with the input-dtype O and L. Returns a dict of CPU float64
+    numpy arrays plus the raw bf16 / fp32 outputs."""
+    qg, kg, vg, dog = to_gpu(q, k, v, do)
+    o32, l32 = fa.forward(qg, kg, vg, causal, scale, o_dtype=torch.float32)
+    o, l = fa.forward(qg, kg, vg, causal, scale)
+    res = {"O32": o32.cpu(), "O": o.cpu(), "L": l.cpu(), "L32": l32.cpu()}
+    if backward:
+        dq, dk, dv = fa.backward(qg, kg, vg, o, l, dog, causal, scale)
+        torch.cuda.synchronize()
+        res.update(dQ=dq.cpu(), dK=dk.cpu(), dV=dv.cpu())
+    del qg, kg, vg, dog
+    return res
+
+
+def check_heads(res, q, k, v, do, causal, dtype, heads, scale=None, grads=True, rows=None,
+                cols=None, tag=""):
+    """Compare the given (b, h) heads of a run with the oracle. rows / cols
+    optionally restrict the compared query rows (O, L, dQ) and key rows
+    (dK, dV). Returns a dict of the worst errors."""
+    tol = TOL[dtype]
+    worst = {}
+    Q, K, V, dO = f64(q), f64(k), f64(v), f64(do)
+    for b, h in heads:
+        ref = oracle.attention_head(Q[b, h], K[b, h], V[b, h], dO[b, h] if grads else None,
+                                    causal, scale, rows=rows, cols=cols)
+        ridx = slice(None) if rows is None else rows
+        cidx = slice(None) if cols is None else cols
+        o_key = "O32" if dtype == "bf16" else "O"
+        e_o = np.abs(f64(res[o_key][b, h])[ridx] - ref["O"]).max()
+        e_l = np.abs(f64(res["L"][b, h])[ridx] - ref["L"]).max()
+        worst["O"] = max(worst.get("O", 0.0), e_o)
+        worst["L"] = max(worst.get("L", 0.0), e_l)
+        assert e_o <= tol["O"], f"{tag} head {(b, h)}: max|dO| {e_o:.3e} > {tol['O']}"
+        assert e_l <= tol["L"], f"{tag} head {(b, h)}: max|dL| {e_l:.3e} > {tol['L']}"
+        if grads:
+            gmax = max(np.abs(ref[n]).max() for n in ("dQ", "dK", "dV"))
+            for name, idx in (("dQ", ridx), ("dK", cidx), ("dV", cidx)):
+                got = f64(res[name][b, h])[idx]
+                want = ref[name]
+                scale_ = max(np.abs(want).max(), 1e-3 * gmax, 1e-30)
+                err = np.abs(got - want).max() / scale_
+                worst[name] = max(worst.get(name, 0.0), err)
+                assert err <= tol["grad"], \
+                    f"{tag} head {(b, h)}: {name} rel err {err:.3e} > {tol['grad']}"
+    if dtype == "bf16":
+        # the bf16 O is the RNE rounding of the fp32 O, bit for bit
+        assert torch.equal(res["O"], res["O32"].to(torch.bfloat16)), f"{tag}: bf16 O != RNE(fp32 O)"
+        assert torch.equal(res["L"], res["L32"]), f"{tag}: L depends on o_dtype"
+    return worst
+
+
+def check_sum_invariants(res, do, dtype, tag=""):
+    """Properties that hold at any size, for every head: the dK rows sum to
+    zero and the dV rows sum to the dO rows (a softmax row sums to one)."""
+    dK, dV = f64(res["dK"]), f64(res["dV"])
+    dO = f64(do)
+    tol = 5e-2 if dtype == "bf16" else 1e-5
+    sum_dk = np.abs(dK.sum(axis=2))                       # [B, H, d]
+    mag_dk = np.abs(dK).sum(axis=2) + 1e-30
+    assert (sum_dk / mag_dk).max() < tol, f"{tag}: sum_j dK_j not ~0"
+    err_dv = np.abs(dV.sum(axis=2) - dO.sum(axis=2))
+    mag_dv = np.abs(dV).sum(axis=2) + 1e-30
+    assert (err_dv / mag_dv).max() < tol, f"{tag}: sum_j dV_j != sum_i dO_i"
+    for name in ("O", "L", "dQ", "dK", "dV"):
+        if name in res:
+            assert torch.isfinite(res[name].float()).all(), f"{tag}: non-finite {name}"

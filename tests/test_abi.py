@@ -1,0 +1,130 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/fa.h declares, and
+reject bad arguments with the documented status codes before any HIP call.
+Only argument-validation paths are exercised here: none of them reaches the
+HIP runtime, so they run on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_tiled_attention_29_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULLPTR, SHAPE, DTYPE, HEADDIM, SCALE, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
+BF16, F32 = 0, 1
+P = 0x1000  # a non-null dummy pointer; never dereferenced on the validation paths
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        pytest.skip("libfa.so not built")
+    return fa.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted(
+        ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version"])
+
+
+def test_library_exports_every_header_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(fa_[a-z_0-9]+)$", out, flags=re.M))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    assert lib.fa_abi_version() == 1
+    for code in range(8):
+        s = fa.fa_status_str(code)
+        assert s and s != "unknown status"
+    assert fa.fa_status_str(99) == "unknown status"
+
+
+def fwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, o_dtype=BF16, lse=P, batch=1, heads=1, n_q=8, n_k=8, d=64,
+                dtype=BF16, causal=0, scale=0.125, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+def bwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, o_dtype=BF16, lse=P, d_o=P, dq=P, dk=P, dv=P, batch=1, heads=1,
+                n_q=8, n_k=8, d=64, dtype=BF16, causal=0, scale=0.125, workspace=P,
+                workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return fa.fa_bwd(**args)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_validation_codes(lib, call):
+    assert call(dtype=7) == DTYPE
+    assert call(o_dtype=5) == DTYPE
+    assert call(dtype=F32, o_dtype=BF16, d=32) == DTYPE
+    assert call(batch=-1) == SHAPE
+    assert call(n_q=-3) == SHAPE
+    assert call(n_k=0) == SHAPE
+    assert call(heads=1 << 20, batch=1 << 12) == SHAPE
+    assert call(d=32) == HEADDIM          # bf16 supports 64 and 128
+    assert call(d=96) == HEADDIM
+    assert call(dtype=F32, o_dtype=F32, d=48) == HEADDIM
+    assert call(scale=0.0) == SCALE
+    assert call(scale=-1.0) == SCALE
+    assert call(scale=float("inf")) == SCALE
+    assert call(scale=float("nan")) == SCALE
+    assert call(q=None) == NULLPTR
+    assert call(v=None) == NULLPTR
+    assert call(lse=None) == NULLPTR
+
+
+def test_backward_specific_codes(lib):
+    assert bwd(d_o=None) == NULLPTR
+    assert bwd(dq=None) == NULLPTR
+    assert bwd(workspace=None) == WORKSPACE
+    need = fa.fa_bwd_workspace_bytes(1, 1, 8, 8, 64, BF16, 0)
+    assert bwd(workspace_bytes=need - 1) == WORKSPACE
+    assert bwd(workspace=P + 4) == WORKSPACE  # not 256-byte aligned
+
+
+def test_empty_forward_is_a_noop(lib):
+    # Nothing to compute: returns before any HIP call, pointers untouched.
+    assert fwd(n_q=0, q=None, o=None, lse=None) == OK
+    assert fwd(batch=0, q=None, k=None, v=None, o=None, lse=None) == OK
+    assert fwd(heads=0, n_k=0) == OK
+
+
+def test_workspace_bytes(lib):
+    def up(x):
+        return (x + 255) // 256 * 256
+    B, H, n_q, n_k, d = 2, 3, 100, 77, 128
+    rows = B * H * n_q
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 1) == up(rows * 4) + up(rows * d * 4)
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 32, F32, 0) == up(rows * 4)
+    assert fa.fa_bwd_workspace_bytes(B, H, 0, n_k, d, BF16, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 96, BF16, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, 0, d, BF16, 0) == 0
+
+
+def test_python_helpers_refuse_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(q, q, q)
+    with pytest.raises(TypeError):
+        fa.forward(q.half(), q.half(), q.half())

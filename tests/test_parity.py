@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every workload is run at its full size in the launch configuration the bench
+times. Heads (or, for the 32K sequence, rows and key columns) are compared
+with the oracle element by element; properties that hold at any size are
+checked on every head. Edge cases cover ragged tails, n_q != n_k under the
+causal mask, single rows/keys, empty calls, degenerate inputs and
+determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import exact_tiled_attention_29_amd as fa
+    from parity import check_heads, check_sum_invariants, f64, run
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+    yield
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_causal"])
+def test_tiny_f32(name):
+    w = WORKLOADS[name]
+    q, k, v, do = make_inputs(w)
+    res = run(q, k, v, do, w.causal)
+    check_heads(res, q, k, v, do, w.causal, "f32", [(0, 0)], tag=name)
+
+
+def test_self_b4h16_n1024_d64():
+    w = WORKLOADS["self_b4h16_n1024_d64"]
+    q, k, v, do = make_inputs(w)
+    res = run(q, k, v, do, w.causal)
+    heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    worst = check_heads(res, q, k, v, do, w.causal, "bf16", heads, tag=w.name)
+    print(w.name, worst)
+    check_sum_invariants(res, do, "bf16", w.name)
+
+
+def test_self_b2h32_n4096_d128_causal():
+    w = WORKLOADS["self_b2h32_n4096_d128_causal"]
+    q, k, v, do = make_inputs(w)
+    res = run(q, k, v, do, w.causal)
+    heads = [(0, 0), (0, 21), (1, 9), (1, 31)]
+    worst = check_heads(res, q, k, v, do, w.causal, "bf16", heads, tag=w.name)
+    print(w.name, worst)
+    check_sum_invariants(res, do, "bf16", w.name)
+
+
+def test_long_b1h8_n32768_d128_causal():
+    w = WORKLOADS["long_b1h8_n32768_d128_causal"]
+    q, k, v, do = make_inputs(w)
+    res = run(q, k, v, do, w.causal)
+    n = w.n_q
+    # first/last rows, tile edges (128, 256, 64-key tiles) and random picks
+    edge = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 4095, 4096, 16383, 16384, n - 129, n - 1]
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([edge, rng.integers(0, n, 48)]))
+    cols = np.unique(np.concatenate([edge, rng.integers(0, n, 48)]))
+    worst = check_heads(res, q, k, v, do, w.causal, "bf16", [(0, 5)], rows=rows, cols=cols,
+                        tag=w.name)
+    print(w.name, worst)
+    check_sum_invariants(res, do, "bf16", w.name)
+
+
+def test_long_forward_only_rows_all_heads():
+    # Forward-only at 32K: sampled rows of every head.
+    w = WORKLOADS["long_b1h8_n32768_d128_causal"]
+    q, k, v, do = make_inputs(w)
+    res = run(q, k, v, do, w.causal, backward=False)
+    rows = np.array([0, 5, 777, 8191, 8192, 20000, 32767])
+    check_heads(res, q, k, v, do, w.causal, "bf16", [(0, h) for h in range(8)], grads=False,
+                rows=rows, tag=w.name + " fwd")
+
+
+def test_cross_b8h12_q1000_k3000_d64():
+    w = WORKLOADS["cross_b8h12_q1000_k3000_d64"]
+    q, k, v, do = make_inputs(w)
+    res = run(q, k, v, do, w.causal)
+    heads = [(0, 0), (2, 5), (4, 11), (7, 3), (7, 11)]
+    worst = check_heads(res, q, k, v, do, w.causal, "bf16", heads, tag=w.name)
+    print(w.name, worst)
+    check_sum_invariants(res, do, "bf16", w.name)
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE = [
+    # (B, H, n_q, n_k, d, dtype, causal)
+    (1, 2, 50, 130, 32, "f32", True),
+    (1, 2, 130, 50, 32, "f32", True),
+    (1, 1, 1, 1, 16, "f32", False),
+    (1, 1, 1, 1, 128, "bf16", True),
+    (1, 2, 1, 300, 64, "bf16", False),
+    (1, 2, 300, 1, 64, "bf16", True),
+    (2, 3, 129, 129, 128, "bf16", True),
+    (1, 2, 257, 255, 128, "bf16", False),
+    (1, 3, 200, 333, 64, "bf16", True),
+    (1, 3, 333, 200, 64, "bf16", True),
+    (1, 2, 700, 700, 128, "bf16", True),
+    (2, 2, 96, 160, 64, "f32", False),
+    (1, 1, 65, 190, 128, "f32", True),
+]
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", EDGE)
+def test_edge_shapes(B, H, n_q, n_k, d, dtype, causal):
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
+    q, k, v, do = make_inputs(w, seed=n_q * 7 + n_k)
+    res = run(q, k, v, do, causal)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    check_heads(res, q, k, v, do, causal, dtype, heads, tag=str((B, H, n_q, n_k, d, dtype, causal)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_page1_backward_demo_shape(causal):
+    # Page 1, section 3 demo: n = 70, d = 16, float32 here, loss sum(O^2) so dO = 2 O.
+    torch.manual_seed(0)
+    q, k, v = (torch.randn(1, 1, 70, 16) for _ in range(3))
+    qg, kg, vg = (t.cuda() for t in (q, k, v))
+    o, l = fa.forward(qg, kg, vg, causal)
+    do = 2 * o
+    res = {"O": o.cpu(), "L": l.cpu()}
+    dq, dk, dv = fa.backward(qg, kg, vg, o, l, do, causal)
+    res.update(dQ=dq.cpu(), dK=dk.cpu(), dV=dv.cpu())
+    check_heads(res, q, k, v, do.cpu(), causal, "f32", [(0, 0)], tag="page1 demo")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_query_gives_mean_of_values(dtype):
+    w = workloads.custom(1, 2, 150, 150, 64, dtype, True)
+    _, k, v, do = make_inputs(w, seed=3)
+    q = torch.zeros_like(k[:, :, :150])
+    res = run(q, k, v, do, True)
+    cnt = np.arange(150) + 1
+    want = np.cumsum(f64(v), axis=2) / cnt[None, None, :, None]
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    assert np.abs(f64(res["O32"]) - want).max() < tol
+    assert np.abs(f64(res["L"]) - np.log(cnt)[None, None]).max() < (1e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_empty_calls():
+    q = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(1, 2, 10, 64, device="cuda").bfloat16()
+    o, l = fa.forward(q, k, k)
+    assert o.shape == (1, 2, 0, 64) and l.shape == (1, 2, 0)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(k, 7.0)
+    dq = torch.empty_like(q)
+    fa.backward(q, k, k, o, l, q, grads=(dq, dk, dv))
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+
+
+def test_forward_is_deterministic():
+    w = workloads.custom(2, 4, 640, 640, 128, "bf16", True)
+    q, k, v, _ = make_inputs(w, seed=1)
+    qg, kg, vg = (t.cuda() for t in (q, k, v))
+    o1, l1 = fa.forward(qg, kg, vg, True)
+    o2, l2 = fa.forward(qg, kg, vg, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_dkdv_deterministic_and_dq_close():
+    w = workloads.custom(1, 4, 512, 512, 64, "bf16", False)
+    q, k, v, do = make_inputs(w, seed=2)
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    o, l = fa.forward(qg, kg, vg)
+    g1 = fa.backward(qg, kg, vg, o, l, dog)
+    g1 = [t.clone() for t in g1]
+    g2 = fa.backward(qg, kg, vg, o, l, dog)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    # dQ sums fp32 partials with atomics in any order: equal up to rounding
+    assert (g1[0].float() - g2[0].float()).abs().max() <= 1e-2 * g1[0].float().abs().max()
+
+
+def test_autograd_wrapper():
+    w = workloads.custom(1, 2, 96, 96, 64, "f32", True)
+    q, k, v, do = make_inputs(w, seed=4)
+    qg, kg, vg = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention(qg, kg, vg, True)
+    o.backward(do.cuda())
+    res = {"O": o.detach().cpu(), "L": fa.forward(qg.detach(), kg.detach(), vg.detach(), True)[1].cpu(),
+           "dQ": qg.grad.cpu(), "dK": kg.grad.cpu(), "dV": vg.grad.cpu()}
+    check_heads(res, q, k, v, do, True, "f32", [(0, 0), (0, 1)], tag="autograd")
+
+
+def test_scale_argument():
+    w = workloads.custom(1, 1, 100, 120, 64, "bf16", False)
+    q, k, v, do = make_inputs(w, seed=5)
+    res = run(q, k, v, do, False, scale=0.05)
+    check_heads(res, q, k, v, do, False, "bf16", [(0, 0)], scale=0.05, tag="scale=0.05")
