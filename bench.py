@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one forward (fa_fwd) plus one backward (fa_bwd: row term D,
+dK/dV/dQ kernel, dQ conversion) over the workload's inputs, which are
+resident in HBM before timing starts. The metric is attention TFLOP/s for
+fwd+bwd with the FLOP convention 4 * n_q * n_k * d per (batch, head) for the
+forward, halved under the causal mask, and 2.5x that for the backward.
+
+Prints one JSON line (the last line of stdout) with the metric, a roofline
+entry for the dominant kernel (its duration measured with HIP events inside
+the timed region) and the fp64 CPU oracle timed on a bounded sample of the
+same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --summarize-pmc DIR      # HBM bytes from rocprofv3 --pmc runs
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # 256 CUs x 4096 FLOP/clk x 2.4 GHz = 2516.6
+METRIC = "attention TFLOP/s fwd+bwd (bf16, causal, n=4096, d=128); % MFMA peak"
+CSRC = os.path.join(ROOT, "exact_tiled_attention_29_amd", "csrc")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_dkdv_self_b2h32_n4096_d128_causal_pmc.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counter runs
+# --------------------------------------------------------------------------
+
+def _read_counter_csv(d):
+    import csv
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_path):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each kernel, scaled by
+    what the counters read for a plain copy kernel of copy_bytes bytes."""
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _read_counter_csv(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_f = [v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy_w = [v for k, v in write.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+    fs = copy_bytes / (max(copy_f) * 1024) if copy_f else 1.0
+    ws = copy_bytes / (max(copy_w) * 1024) if copy_w else 1.0
+    lines = [f"source_hash {kernel_source_hash()}",
+             f"copy_bytes {copy_bytes} fetch_scale {fs:.4f} write_scale {ws:.4f}"]
+    for k in sorted(set(fetch) | set(write)):
+        f_ = fetch.get(k, float("nan")) * 1024 * fs
+        w_ = write.get(k, float("nan")) * 1024 * ws
+        lines.append(f"kernel {k[:120]!r} fetch_bytes {f_:.0f} write_bytes {w_:.0f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_from_summary(kernel_key):
+    """HBM bytes per launch of the kernel, or None when no summary exists or
+    the kernels changed since the counters were taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    lines = open(PMC_SUMMARY).read().splitlines()
+    src = next((l.split()[1] for l in lines if l.startswith("source_hash")), None)
+    if src != kernel_source_hash():
+        return None
+    for l in lines:
+        if l.startswith("kernel") and kernel_key in l:
+            parts = l.split()
+            return float(parts[parts.index("fetch_bytes") + 1]) + float(parts[parts.index("write_bytes") + 1])
+    return None
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample
+# --------------------------------------------------------------------------
+
+def cpu_baseline(w, q, k, v, do, n_heads):
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    picks = [(i % w.batch, (i * 7) % w.heads) for i in range(n_heads)]
+    t0 = time.perf_counter()
+    for b, h in picks:
+        oracle.attention_head(f(q[b, h]), f(k[b, h]), f(v[b, h]), f(do[b, h]), w.causal)
+    dt = time.perf_counter() - t0
+    flop = w.fwd_bwd_flop() / (w.batch * w.heads) * len(picks)
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{len(picks)} of {w.batch * w.heads} heads of {w.name}, fwd+bwd in fp64 "
+                  f"({dt:.1f} s; metric FLOP convention)",
+        "seconds": dt,
+    }
+
+
+# --------------------------------------------------------------------------
+# GPU benchmark
+# --------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads the oracle baseline runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summary-out", default=PMC_SUMMARY)
+    ap.add_argument("--summary-copy-mib", type=int, default=512)
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summary_copy_mib << 20,
+                      args.summary_out)
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the attention path is benchmarked on a single "
+              "MI355X (heads shard across GPUs with no communication); use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_tiled_attention_29_amd as fa
+    import workloads
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] workload {w.name}: B={w.batch} H={w.heads} n_q={w.n_q} n_k={w.n_k} d={w.d} "
+        f"{w.dtype} causal={w.causal}")
+    q, k, v, do = workloads.make_inputs(w)
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o = torch.empty_like(qg)
+    lse = torch.empty(w.batch, w.heads, w.n_q, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+    ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.d,
+                                                      fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32,
+                                                      w.causal)), dtype=torch.uint8, device=dev)
+
+    if args.copy_mib:
+        a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(evf=None, evb=None):
+        if evf is not None:
+            evf[0].record()
+        fa.forward(qg, kg, vg, w.causal, out=o, lse=lse)
+        if evf is not None:
+            evf[1].record()
+        fa.backward(qg, kg, vg, o, lse, dog, w.causal, workspace=ws, grads=(dq, dk, dv), events=evb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evf = [[E(), E()] for _ in range(K)]
+    evb = [[E(), E(), E(), E()] for _ in range(K)]
+    for e in evb:                      # create the events before the timed region
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evf[i], evb[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = lambda a, b: a.elapsed_time(b)  # noqa: E731
+    t_fwd = sum(ms(*e) for e in evf) / K
+    t_pre = sum(ms(e[0], e[1]) for e in evb) / K
+    t_dkdv = sum(ms(e[1], e[2]) for e in evb) / K
+    t_conv = sum(ms(e[2], e[3]) for e in evb) / K
+    ms_step = wall * 1e3 / K
+
+    f_fwd = w.fwd_flop()
+    f_bwd = 2.5 * f_fwd
+    f_all = w.fwd_bwd_flop()
+    value = f_all / (ms_step * 1e-3) / 1e12
+    kernels = {"fwd": t_fwd, "bwd_pre": t_pre, "bwd_dkdv": t_dkdv, "bwd_dq_convert": t_conv}
+    dom = max(kernels, key=kernels.get)
+    dom_flop = {"fwd": f_fwd, "bwd_dkdv": f_bwd}.get(dom)
+    if dom_flop is not None:
+        ach = dom_flop / (kernels[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_summary("dkdv" if dom == "bwd_dkdv" else "fwd_bf16"),
+                "kernel": dom, "avg_ms": round(kernels[dom], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": 8000.0, "unit": "GB/s", "frac": None,
+                "traffic": None, "kernel": dom, "avg_ms": round(kernels[dom], 4)}
+
+    log(f"[bench] {K} steps: {ms_step:.4f} ms/step -> {value:.1f} TFLOP/s "
+        f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.1f})")
+    for kname, t in kernels.items():
+        log(f"[bench]   {kname:15s} {t:.4f} ms")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, workloads.py)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n_q": w.n_q,
+                   "n_k": w.n_k, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((t_pre + t_dkdv + t_conv) * 1e-3) / 1e12, 2),
+        "kernel_ms": {k_: round(t, 4) for k_, t in kernels.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle on {args.cpu_heads} heads ...")
+        cb = cpu_baseline(w, q, k, v, do, args.cpu_heads)
+        log(f"[bench] oracle: {cb['value']:.4f} TFLOP/s on {cb['cores']} threads ({cb['seconds']:.1f} s)")
+        cb.pop("seconds")
+        result["cpu_baseline"] = cb
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -21,7 +21,7 @@ import torch  # imported before libfa.so so the process shares torch's HIP runti
 
 __all__ = [
     "FA_BF16", "FA_F32", "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version",
+    "fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version",
     "forward", "backward", "FlashAttention", "attention",
 ]
 
@@ -62,6 +62,8 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                            i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_timed.argtypes = lib.fa_bwd.argtypes + [vp]
+    lib.fa_bwd_timed.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -84,6 +86,13 @@ def fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d,
     return load_library().fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q,
                                  n_k, d, dtype, int(causal), float(scale), workspace,
                                  workspace_bytes, stream)
+
+
+def fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype,
+                 causal, scale, workspace, workspace_bytes, stream, events):
+    return load_library().fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads,
+                                       n_q, n_k, d, dtype, int(causal), float(scale), workspace,
+                                       workspace_bytes, stream, events)
 
 
 def fa_bwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, causal):
@@ -128,6 +137,13 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _event_handle(e) -> int:
+    """hipEvent_t of a torch.cuda.Event (torch creates it on first record)."""
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
+
+
 def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None):
     """O, L = attention(q, k, v). q: [B,H,n_q,d]; k, v: [B,H,n_k,d].
 
@@ -156,8 +172,12 @@ def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None)
     return out, lse
 
 
-def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grads=None):
-    """dQ, dK, dV from the forward's O and L and the upstream gradient dO."""
+def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grads=None,
+             events=None):
+    """dQ, dK, dV from the forward's O and L and the upstream gradient dO.
+
+    events: optional 4 torch.cuda.Event(enable_timing=True), recorded on the
+    current stream around the backward's three kernels (see fa_bwd_timed)."""
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
     dt = _code(q.dtype)
@@ -175,10 +195,15 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _code(o.dtype),
-                lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                B, H, n_q, n_k, d, dt, causal, scale, workspace.data_ptr(), workspace.numel(),
-                _stream(q.device))
+    ev = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events must hold 4 torch.cuda.Event")
+        ev = (ctypes.c_void_p * 4)(*[_event_handle(e) for e in events])
+    st = fa_bwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _code(o.dtype),
+                      lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      B, H, n_q, n_k, d, dt, causal, scale, workspace.data_ptr(), workspace.numel(),
+                      _stream(q.device), ev)
     if st != 0:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv

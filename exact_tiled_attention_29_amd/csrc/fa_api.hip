@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_launch.h"
 
 namespace {
@@ -41,8 +41,9 @@ int check_common(int batch, int heads, int n_q, int n_k, int d, int dtype, int o
 
 size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
     const size_t rows = (size_t)bh * (size_t)n_q;
-    size_t b = align_up(rows * sizeof(float));                     // D
-    if (dtype == FA_BF16) b += align_up(rows * (size_t)d * sizeof(float));  // dQ accumulator
+    size_t b = align_up(rows * sizeof(float));  // D
+    if (dtype == FA_BF16)                       // dQ accumulator, rows padded per head
+        b += align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * (size_t)d * sizeof(float));
     return b;
 }
 
@@ -93,10 +94,11 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int
     return workspace_bytes((long long)batch * heads, n_q, d, dtype);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
-           const float* lse, const void* d_o, void* dq, void* dk, void* dv,
-           int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
-           void* workspace, size_t workspace_bytes_given, void* stream) {
+int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                 const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                 int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+                 void* workspace, size_t workspace_bytes_given, void* stream,
+                 void* const* events) {
     bool empty = false;
     int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, scale, &empty);
     if (st != FA_OK) return st;
@@ -120,22 +122,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, int o_dty
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.bh = (int)bh; a.n_q = n_q; a.n_k = n_k; a.d = d;
     a.causal = causal != 0; a.o_f32 = o_dtype == FA_F32; a.scale = scale;
+    a.events = (hipEvent_t const*)events;
     char* w = (char*)workspace;
     a.drow = (float*)w;
     a.dq_acc = dtype == FA_BF16 ? (float*)(w + align_up((size_t)bh * n_q * sizeof(float))) : nullptr;
     return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
 
-}  // extern "C"
-
-namespace fa {
-
-int fwd_bf16_qb_override() {
-    static const int v = [] {
-        const char* e = getenv("FA_FWD_QB");
-        return e ? atoi(e) : 0;
-    }();
-    return v;
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+           const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+           int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+           void* workspace, size_t workspace_bytes_given, void* stream) {
+    return fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d,
+                        dtype, causal, scale, workspace, workspace_bytes_given, stream, nullptr);
 }
 
-}  // namespace fa
+}  // extern "C"
+

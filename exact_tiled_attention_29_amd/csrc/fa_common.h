@@ -73,6 +73,57 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
     return z;
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations: global
+// loads and atomics still in flight are not waited for (a __syncthreads()
+// would also drain every outstanding global store and atomic).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, the lane with local index
+// 4*a + e receives element e of the 8-byte chunks addressed by the lanes
+// a, 4 + a, 8 + a, 12 + a (in that order). When lane s of the group points
+// at row k0 + s/4, column n0 + 4*(s%4) of a row-major bf16 tile, lane t
+// therefore receives column n0 + t, rows k0 .. k0 + 3: an MFMA operand with
+// the contraction index along the registers, read from an untransposed tile.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) lds_bf16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+    return r;
+}
+
+// XOR swizzle of the 16-byte chunks of a row-major bf16 tile with rows of D
+// elements (D/8 chunks): row rho keeps logical chunk c at physical chunk
+// c ^ tile_swz<D>(rho). Chosen so that (a) 16 consecutive rows read at one
+// logical chunk (an MFMA operand read with ds_read_b128) hit 16 different
+// bank groups, and (b) 4 consecutive rows (aligned to 4) read over 4
+// consecutive chunks (a transpose read) hit disjoint banks.
+template <int D>
+__device__ __forceinline__ int tile_swz(int rho) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 128) return (4 * (rho & 3)) ^ ((rho >> 2) & 3);
+    else return (4 * ((rho >> 1) & 1)) ^ ((rho >> 2) & 3);
+}
+
+// Element offset of (row, col) in a swizzled row-major tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    return row * D + 8 * ((col >> 3) ^ tile_swz<D>(row)) + (col & 7);
+}
+
+// 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16*l; lds_base must be wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
 // Map a hardware workgroup index to a logical one so that each of the 8
 // XCDs (which receive workgroups round-robin: id % 8) works through one
 // contiguous range of logical ids. Bijective for any n.

@@ -246,20 +246,25 @@ hipError_t bwd_launch(const BwdArgs& a, hipStream_t st) {
     const int nkt = (a.n_k + kRows - 1) / kRows;
     if (nb > 0x7fffffffLL || (long long)a.bh * nqt > 0x7fffffffLL || (long long)a.bh * nkt > 0x7fffffffLL)
         return hipErrorInvalidValue;
+    hipError_t e = record_stage(a, 0, st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)nb), dim3(256), 0, st,
                        (const float*)a.o, (const float*)a.d_o, a.drow, rows);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = record_stage(a, 1, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkt)), dim3(kRows), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.d_o,
                        a.lse, a.drow, (float*)a.dk, (float*)a.dv, a.n_q, a.n_k, nkt, a.scale,
                        a.scale * kLog2e);
     e = hipGetLastError();
+    if (e == hipSuccess) e = record_stage(a, 2, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqt)), dim3(kRows), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.d_o,
                        a.lse, a.drow, (float*)a.dq, a.n_q, a.n_k, nqt, a.scale, a.scale * kLog2e);
-    return hipGetLastError();
+    e = hipGetLastError();
+    return e == hipSuccess ? record_stage(a, 3, st) : e;
 }
 
 template <int D>

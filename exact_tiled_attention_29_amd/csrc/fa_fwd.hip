@@ -9,16 +9,18 @@
 // the one of page 1, section 1 and page 3 ("Flash Attention"), section 1.1.
 //
 // MI355X mapping (not from the pages):
-//  * one workgroup = 4 waves = 128*QB query rows of one (batch, head);
-//    each wave owns 32*QB rows and keeps its Q rows in registers as the
-//    B operand of S^T = K Q^T, so every per-row quantity (m, l, the O
-//    accumulator column) lives in one lane pair (l, l^32);
-//  * K tiles (64 keys, row-major) and V^T tiles (keys contiguous, permuted
-//    so each MFMA A operand is one 16-byte LDS read) are double-buffered in
-//    LDS; the next tile's global loads are in flight during the MFMAs;
+//  * one workgroup = 4 waves = 128 query rows of one (batch, head), two
+//    workgroups per CU; each wave owns 32 rows and keeps its Q rows in
+//    registers as the B operand of S^T = K Q^T, so every per-row quantity
+//    (m, l, the O accumulator column) lives in one lane pair (l, l^32);
+//  * K and V tiles (64 keys, row-major, swizzled 16-byte chunks) are copied
+//    global -> LDS without registers and double-buffered; the V^T operand of
+//    O^T += V^T P^T comes from transpose reads of the row-major V tile;
 //  * scores are kept in the exp2 domain (scale * log2 e folded in), the
 //    row max needs one cross-lane step (v_permlane32_swap), l sums the fp32
-//    probabilities and only the PV operand is rounded to bf16 (RNE);
+//    probabilities and only the PV operand is rounded to bf16 (RNE); O and l
+//    are rescaled only when a row max grows by more than 2^8 (exact: O and l
+//    share the reference max, and O / l does not depend on it);
 //  * workgroups are renumbered so each XCD works through whole heads
 //    (K/V reuse in that XCD's L2), longest causal tiles first.
 #include "fa_common.h"
@@ -31,31 +33,29 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBC = 64;  // keys per tile
 
-// V^T rows hold each 16-key chunk permuted: position 8*h + 4*i + j holds key
-// 8*i + 4*h + j (h, i in {0,1}, j in 0..3). Lane-half g of the PV MFMA needs
-// the keys its S^T accumulator rows cover, {4g..4g+3, 8+4g..8+4g+3}, and
-// finds them at positions 8g..8g+7: one 16-byte LDS read.
-
-template <int D, int QB, bool CAUSAL, bool OF32>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
+template <int D, bool CAUSAL, bool OF32>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ Lse,
     int n_q, int n_k, int n_qtiles, float scale2) {
-    constexpr int RW = 32 * QB;          // query rows per wave
+    constexpr int RW = 32;               // query rows per wave
     constexpr int BR = 4 * RW;           // query rows per workgroup
     constexpr int KK = D / 16;           // MFMA k-steps over d
     constexpr int NDB = D / 32;          // 32-wide d blocks of the output
-    constexpr int KSTR = D + 8;          // K tile row stride (elements)
-    constexpr int VSTR = kBC + 8;        // V^T tile row stride (elements)
-    constexpr int CK = kBC * D / 8 / kThreads;  // 16-byte K chunks per thread
-    constexpr int DPT = D / 32;          // d columns per thread in the V^T stage
-    static_assert(CK >= 1 && DPT >= 2, "tile shape");
+    constexpr int TILE = kBC * D;        // elements per K or V tile
+    constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KB direct loads per wave per tile
+    constexpr float kTau = 8.0f;         // rescale O only when the max grows by > 2^kTau
 
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBC * KSTR];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * VSTR];
+    // One LDS object per buffer, so the compiler can tell the tile being
+    // read from the one being filled and need not wait for the copies.
+    __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+    const int s16 = lane & 15, half = (lane >> 4) & 1;
 
     const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
     const int bh = logical / n_qtiles;
@@ -68,225 +68,183 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
     const bf16* Vh = V + (size_t)bh * n_k * D;
 
     // Q rows as MFMA B operands: lane (r, g) holds d = 16*kk + 8*g .. +7.
-    bf16x8 qreg[QB][KK];
+    bf16x8 qreg[KK];
+    {
+        const int row = qw + r;
+        const int rc = min(row, n_q - 1);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = qw + 32 * qb + r;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qreg[qb][kk] = row < n_q ? *(const bf16x8*)(Qh + (size_t)row * D + 16 * kk + 8 * g)
-                                     : zero_bf16x8();
+        for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 x = *(const bf16x8*)(Qh + rc * D + 16 * kk + 8 * g);
+            qreg[kk] = row < n_q ? x : zero_bf16x8();
+        }
     }
 
     int kend = n_k;
     if (CAUSAL) kend = min(n_k, min(q0 + BR, n_q));  // keys <= last row of the tile
     const int ntiles = (kend + kBC - 1) / kBC;
 
-    // ---- tile staging (registers -> LDS) ----
-    uint4 kst[CK];
-    typedef __attribute__((ext_vector_type(DPT / 2))) unsigned vword_t;
-    vword_t vst[8];
-    const int vdg = tid & 31;   // d group of DPT columns
-    const int voct = tid >> 5;  // key octet: chunk voct/2, half voct%2
-
-    auto load_tile = [&](int ks) {
+    // K and V tiles go straight from global memory to LDS (no registers),
+    // row-major with swizzled 16-byte chunks. Each wave copies LPW blocks of
+    // 1 KB: lane l of block b fills chunk position 64*b + l. Rows past n_k
+    // read row n_k - 1 (finite data; those keys are masked).
+    auto issue_tile = [&](bf16* Kd, bf16* Vd, int ks) {
 #pragma unroll
-        for (int i = 0; i < CK; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c / (D / 8), cc = c % (D / 8);
-            const int key = ks + row;
-            kst[i] = key < n_k ? *(const uint4*)(Kh + (size_t)key * D + 8 * cc) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int key = ks + 16 * (voct >> 1) + 8 * (e >> 2) + 4 * (voct & 1) + (e & 3);
-            if (key < n_k) {
-                vst[e] = *(const vword_t*)(Vh + (size_t)key * D + DPT * vdg);
-            } else {
-#pragma unroll
-                for (int w = 0; w < DPT / 2; ++w) vst[e][w] = 0u;
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CK; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c / (D / 8), cc = c % (D / 8);
-            *(uint4*)(&Ks[buf][row * KSTR + 8 * cc]) = kst[i];
-        }
-        // Transpose 8 keys x DPT columns into DPT rows of 8 keys.
-#pragma unroll
-        for (int dd = 0; dd < DPT; ++dd) {
-            const int w = dd >> 1, sh = 16 * (dd & 1);
-            unsigned h[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = (vst[e][w] >> sh) & 0xffffu;
-            uint4 pk = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                  h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-            *(uint4*)(&Vt[buf][(DPT * vdg + dd) * VSTR + 16 * (voct >> 1) + 8 * (voct & 1)]) = pk;
+        for (int i = 0; i < LPW; ++i) {
+            const int b = 4 * i + wave;
+            const int p = 64 * b + lane;
+            const int row = p / (D / 8), pc = p % (D / 8);
+            const int chunk = pc ^ tile_swz<D>(row);
+            const int goff = min(ks + row, n_k - 1) * D + 8 * chunk;
+            load_lds16(Kh + goff, Kd + 512 * b);
+            load_lds16(Vh + goff, Vd + 512 * b);
         }
     };
 
-    float m_run[QB], l_run[QB];
-    f32x16 o[QB][NDB];
+    float m_ref = kNegInf, l_run = 0.0f;
+    f32x16 o[NDB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_run[qb] = kNegInf;
-        l_run[qb] = 0.0f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[qb][db] = zero_f32x16();
-    }
+    for (int db = 0; db < NDB; ++db) o[db] = zero_f32x16();
 
     const int wave_last_row = min(qw + RW, n_q) - 1;  // < qw when the wave has no rows
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const int ks = t * kBC;
-        const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(ks + kBC);
-
+    // Compute on one staged tile (K rows in Kb, V rows in Vb).
+    auto tile_step = [&](const bf16* Kb, const bf16* Vb, int ks) {
         const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row);
         if (active) {
             // S^T (keys x queries) for two 32-key blocks.
-            f32x16 s[QB][2];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][0] = s[qb][1] = zero_f32x16();
+            f32x16 s[2];
+            s[0] = s[1] = zero_f32x16();
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 a = *(const bf16x8*)(&Ks[buf][(32 * kb + r) * KSTR + 16 * kk + 8 * g]);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qreg[qb][kk], s[qb][kb]);
+                    const bf16x8 a = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 16 * kk + 8 * g)]);
+                    s[kb] = mfma32(a, qreg[kk], s[kb]);
                 }
             }
             // Mask: keys past n_k, and (causal) keys after the query.
             const bool need_mask = (ks + kBC > n_k) || (CAUSAL && ks + kBC - 1 > qw);
             if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int row = qw + 32 * qb + r;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int key = ks + 32 * kb + acc_row(v, g);
-                            if (key >= n_k || (CAUSAL && key > row)) s[qb][kb][v] = kNegInf;
-                        }
-                }
-            }
-            // Online softmax; P packed as bf16 B operands, 4 chunks of 16 keys.
-            bf16x8 pb[QB][4];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = kNegInf;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][kb][v]);
-                mx = halves_max(mx);
-                const float m_new = fmaxf(m_run[qb], mx * scale2);
-                const float m_use = m_new == kNegInf ? 0.0f : m_new;
-                const float corr = fast_exp2(m_run[qb] - m_use);
-                float rs = 0.0f;
+                const int row = qw + r;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const float p = fast_exp2(fmaf(s[qb][kb][v], scale2, -m_use));
-                        rs += p;
-                        pb[qb][2 * kb + (v >> 3)][v & 7] = to_bf16(p);
+                        const int key = ks + 32 * kb + acc_row(v, g);
+                        if (key >= n_k || (CAUSAL && key > row)) s[kb][v] = kNegInf;
                     }
-                l_run[qb] = l_run[qb] * corr + rs;
-                m_run[qb] = m_new;
+            }
+            // Online softmax in the exp2 domain against a reference max m_ref
+            // that only moves when the row max exceeds it by more than 2^kTau;
+            // O and l are rescaled only then (a wave-wide decision).
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+            mx = halves_max(mx) * scale2;
+            if (__any(mx > m_ref + kTau)) {
+                const float m_new = fmaxf(m_ref, mx);
+                const float corr = fast_exp2(m_ref - (m_new == kNegInf ? 0.0f : m_new));
+                l_run *= corr;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) o[qb][db][v] *= corr;
+                    for (int v = 0; v < 16; ++v) o[db][v] *= corr;
+                m_ref = m_new;
             }
-            // O^T (d x queries) += V^T P^T.
+            const float m_use = m_ref == kNegInf ? 0.0f : m_ref;
+            bf16x8 pb[4];
+            float rs = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float p = fast_exp2(fmaf(s[kb][v], scale2, -m_use));
+                    rs += p;
+                    pb[2 * kb + (v >> 3)][v & 7] = to_bf16(p);
+                }
+            l_run += rs;
+            // O^T (d x queries) += V^T P^T; V^T operands by transpose reads.
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 a = *(const bf16x8*)(&Vt[buf][(32 * db + r) * VSTR + 16 * c + 8 * g]);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, pb[qb][c], o[qb][db]);
+                    const int col = 32 * db + 16 * half + 4 * (s16 & 3);
+                    const int row0 = 16 * c + 4 * g + (s16 >> 2);
+                    const bf16x8 a = concat(lds_read_tr(&Vb[tile_off<D>(row0, col)]),
+                                            lds_read_tr(&Vb[tile_off<D>(row0 + 8, col)]));
+                    o[db] = mfma32(a, pb[c], o[db]);
                 }
             }
         }
-        if (has_next) store_tile(buf ^ 1);
+    };
+
+    issue_tile(Ks0, Vs0, 0);
+    __syncthreads();
+    // Unrolled by two so each step names its buffers at compile time.
+    for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles) issue_tile(Ks1, Vs1, (t + 1) * kBC);
+        tile_step(Ks0, Vs0, t * kBC);
+        __syncthreads();  // tile t+1 landed (each wave waited for its copies); tile t reads done
+        if (t + 1 >= ntiles) break;
+        if (t + 2 < ntiles) issue_tile(Ks0, Vs0, (t + 2) * kBC);
+        tile_step(Ks1, Vs1, (t + 1) * kBC);
         __syncthreads();
     }
 
     // Epilogue: O / l, L = ln 2 * (m + log2 l).
+    const float l = halves_sum(l_run);
+    const int row = qw + r;
+    if (row < n_q) {
+        const float inv = 1.0f / l;
+        const size_t obase = ((size_t)bh * n_q + row) * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l = halves_sum(l_run[qb]);
-        const int row = qw + 32 * qb + r;
-        if (row < n_q) {
-            const float inv = 1.0f / l;
-            const size_t obase = ((size_t)bh * n_q + row) * D;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int d0 = 32 * db + 8 * i + 4 * g;
-                    const float x0 = o[qb][db][4 * i + 0] * inv, x1 = o[qb][db][4 * i + 1] * inv;
-                    const float x2 = o[qb][db][4 * i + 2] * inv, x3 = o[qb][db][4 * i + 3] * inv;
-                    if (OF32) {
-                        *(float4*)((float*)Out + obase + d0) = make_float4(x0, x1, x2, x3);
-                    } else {
-                        bf16x4 pk;
-                        pk[0] = to_bf16(x0); pk[1] = to_bf16(x1); pk[2] = to_bf16(x2); pk[3] = to_bf16(x3);
-                        *(bf16x4*)((bf16*)Out + obase + d0) = pk;
-                    }
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * g;
+                const float x0 = o[db][4 * i + 0] * inv, x1 = o[db][4 * i + 1] * inv;
+                const float x2 = o[db][4 * i + 2] * inv, x3 = o[db][4 * i + 3] * inv;
+                if (OF32) {
+                    *(float4*)((float*)Out + obase + d0) = make_float4(x0, x1, x2, x3);
+                } else {
+                    bf16x4 pk;
+                    pk[0] = to_bf16(x0); pk[1] = to_bf16(x1); pk[2] = to_bf16(x2); pk[3] = to_bf16(x3);
+                    *(bf16x4*)((bf16*)Out + obase + d0) = pk;
                 }
-            if (g == 0) Lse[(size_t)bh * n_q + row] = kLn2 * (m_run[qb] + fast_log2(l));
-        }
+            }
+        if (g == 0) Lse[(size_t)bh * n_q + row] = kLn2 * (m_ref + fast_log2(l));
     }
 }
 
-template <int D, int QB, bool CAUSAL, bool OF32>
+template <int D, bool CAUSAL, bool OF32>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
-    constexpr int BR = 128 * QB;
+    constexpr int BR = 128;
     const int n_qtiles = (a.n_q + BR - 1) / BR;
     const long long nwg = (long long)a.bh * n_qtiles;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, CAUSAL, OF32>), dim3((unsigned)nwg), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OF32>), dim3((unsigned)nwg), dim3(kThreads), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o, a.lse,
                        a.n_q, a.n_k, n_qtiles, a.scale * kLog2e);
     return hipGetLastError();
 }
 
-template <int D, int QB>
+template <int D>
 hipError_t dispatch_mask(const FwdArgs& a, hipStream_t st) {
     if (a.causal)
-        return a.o_f32 ? launch<D, QB, true, true>(a, st) : launch<D, QB, true, false>(a, st);
-    return a.o_f32 ? launch<D, QB, false, true>(a, st) : launch<D, QB, false, false>(a, st);
+        return a.o_f32 ? launch<D, true, true>(a, st) : launch<D, true, false>(a, st);
+    return a.o_f32 ? launch<D, false, true>(a, st) : launch<D, false, false>(a, st);
 }
 
 }  // namespace
 
-int fwd_bf16_rows_per_wg(const FwdArgs& a) {
-    // Two 32-row blocks per wave halve the LDS operand traffic per MFMA but
-    // need enough tiles to fill 256 CUs.
-    const int qb = fwd_bf16_qb_override();
-    if (qb == 1 || qb == 2) return 128 * qb;
-    const long long wg2 = (long long)a.bh * ((a.n_q + 255) / 256);
-    return wg2 >= 512 ? 256 : 128;
-}
+int fwd_bf16_rows_per_wg(const FwdArgs&) { return 128; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
-    const bool two = fwd_bf16_rows_per_wg(a) == 256;
     switch (a.d) {
-        case 64: return two ? dispatch_mask<64, 2>(a, st) : dispatch_mask<64, 1>(a, st);
-        case 128: return two ? dispatch_mask<128, 2>(a, st) : dispatch_mask<128, 1>(a, st);
+        case 64: return dispatch_mask<64>(a, st);
+        case 128: return dispatch_mask<128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -37,7 +37,18 @@ struct BwdArgs {
     float scale;
     float* dq_acc;  // fp32 [bh, n_q, d] (bf16 path only)
     float* drow;    // fp32 [bh, n_q]: D = rowsum(dO * O)
+    hipEvent_t const* events;  // NULL or 4 events: before D, before dK/dV, after dK/dV, end
 };
+
+// Record stage event i of a backward call (no-op without events).
+inline hipError_t record_stage(const BwdArgs& a, int i, hipStream_t st) {
+    return a.events ? hipEventRecord(a.events[i], st) : hipSuccess;
+}
+
+// Rows per head of the bf16 backward's fp32 dQ accumulator: n_q rounded up
+// to the 32-row query tile, so the dK/dV kernel's atomic adds need no row
+// guard (the padding rows are scratch and never read back).
+inline int dq_rows_padded(int n_q) { return (n_q + 31) / 32 * 32; }
 
 // bf16 path (MFMA).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
@@ -52,8 +63,5 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st);
 // so the call is safe under stream capture.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
-// Tuning override read once from the environment (FA_FWD_QB = 1 or 2);
-// 0 when unset. Used by the sweep in the bench harness.
-int fwd_bf16_qb_override();
 
 }  // namespace fa

@@ -75,8 +75,9 @@ int fa_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (0 for an empty
- * call). bf16: an fp32 dQ accumulator [B,H,n_q,d] plus the fp32 row term
- * D [B,H,n_q]; float32: D only. Returns 0 for arguments fa_bwd would reject.
+ * call). bf16: the fp32 row term D [B,H,n_q] plus an fp32 dQ accumulator
+ * [B,H,ceil(n_q/32)*32,d] (each 256-byte aligned); float32: D only.
+ * Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
                               int dtype, int causal);
@@ -107,6 +108,23 @@ int fa_bwd(const void* q, const void* k, const void* v,
            int batch, int heads, int n_q, int n_k, int d, int dtype,
            int causal, float scale,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd with per-kernel timing: identical arguments and results, plus
+ * `events`, NULL or an array of 4 hipEvent_t (passed as void*) created by
+ * the caller with timing enabled. They are recorded on `stream` before the
+ * row-term kernel (D = rowsum(dO * O)), before the dK/dV kernel, after it,
+ * and after the last kernel, so hipEventElapsedTime gives each stage's
+ * duration. For the callers that need the dominant kernel's own time (the
+ * benchmark); the computation is the one fa_bwd documents.
+ */
+int fa_bwd_timed(const void* q, const void* k, const void* v,
+                 const void* o, int o_dtype, const float* lse, const void* d_o,
+                 void* dq, void* dk, void* dv,
+                 int batch, int heads, int n_q, int n_k, int d, int dtype,
+                 int causal, float scale,
+                 void* workspace, size_t workspace_bytes, void* stream,
+                 void* const* events);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);

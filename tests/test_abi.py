@@ -37,7 +37,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version"])
+        ["fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_status_str",
+         "fa_abi_version"])
 
 
 def test_library_exports_every_header_function(lib):
@@ -114,7 +115,8 @@ def test_workspace_bytes(lib):
         return (x + 255) // 256 * 256
     B, H, n_q, n_k, d = 2, 3, 100, 77, 128
     rows = B * H * n_q
-    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 1) == up(rows * 4) + up(rows * d * 4)
+    pad = (n_q + 31) // 32 * 32
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 1) == up(rows * 4) + up(B * H * pad * d * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 32, F32, 0) == up(rows * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, 0, n_k, d, BF16, 0) == 0
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 96, BF16, 0) == 0
