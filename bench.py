@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one forward (fa_fwd) plus one backward (fa_bwd: row term D,
-dK/dV/dQ kernel, dQ conversion) over the workload's inputs, which are
+One step = one forward (fa_fwd) plus one backward (fa_bwd: row-term
+kernel, dK/dV kernel, dQ kernel) over the workload's inputs, which are
 resident in HBM before timing starts. The metric is attention TFLOP/s for
 fwd+bwd with the FLOP convention 4 * n_q * n_k * d per (batch, head) for the
 forward, halved under the causal mask, and 2.5x that for the backward.
@@ -219,21 +219,25 @@ def main():
     t_fwd = sum(ms(*e) for e in evf) / K
     t_pre = sum(ms(e[0], e[1]) for e in evb) / K
     t_dkdv = sum(ms(e[1], e[2]) for e in evb) / K
-    t_conv = sum(ms(e[2], e[3]) for e in evb) / K
+    t_dq = sum(ms(e[2], e[3]) for e in evb) / K
     ms_step = wall * 1e3 / K
 
     f_fwd = w.fwd_flop()
     f_bwd = 2.5 * f_fwd
     f_all = w.fwd_bwd_flop()
     value = f_all / (ms_step * 1e-3) / 1e12
-    kernels = {"fwd": t_fwd, "bwd_pre": t_pre, "bwd_dkdv": t_dkdv, "bwd_dq_convert": t_conv}
+    kernels = {"fwd": t_fwd, "bwd_pre": t_pre, "bwd_dkdv": t_dkdv, "bwd_dq": t_dq}
     dom = max(kernels, key=kernels.get)
-    dom_flop = {"fwd": f_fwd, "bwd_dkdv": f_bwd}.get(dom)
+    # FLOPs each kernel's products need: forward S and PV (2 products); dK/dV
+    # kernel S, dP, dV, dK (4); dQ kernel S, dP recomputed and dQ (3). One
+    # product over all (b, h) is half the forward count.
+    dom_flop = {"fwd": f_fwd, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 1.5 * f_fwd}.get(dom)
     if dom_flop is not None:
         ach = dom_flop / (kernels[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_summary("dkdv" if dom == "bwd_dkdv" else "fwd_bf16"),
+                "traffic": traffic_from_summary({"fwd": "fwd_bf16", "bwd_dkdv": "bwd_dkdv",
+                                                 "bwd_dq": "bwd_dq_kernel"}[dom]),
                 "kernel": dom, "avg_ms": round(kernels[dom], 4)}
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": 8000.0, "unit": "GB/s", "frac": None,
@@ -253,7 +257,7 @@ def main():
                    "n_k": w.n_k, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / ((t_pre + t_dkdv + t_conv) * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((t_pre + t_dkdv + t_dq) * 1e-3) / 1e12, 2),
         "kernel_ms": {k_: round(t, 4) for k_, t in kernels.items()},
         "roofline": roof,
     }

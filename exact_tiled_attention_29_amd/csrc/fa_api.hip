@@ -40,11 +40,10 @@ int check_common(int batch, int heads, int n_q, int n_k, int d, int dtype, int o
 }
 
 size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
-    const size_t rows = (size_t)bh * (size_t)n_q;
-    size_t b = align_up(rows * sizeof(float));  // D
-    if (dtype == FA_BF16)                       // dQ accumulator, rows padded per head
-        b += align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * (size_t)d * sizeof(float));
-    return b;
+    (void)d;
+    if (dtype == FA_F32) return align_up((size_t)bh * (size_t)n_q * sizeof(float));  // D
+    // bf16: D and L * log2(e), rows padded per head to a multiple of 32
+    return 2 * align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * sizeof(float));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
@@ -125,7 +124,9 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int
     a.events = (hipEvent_t const*)events;
     char* w = (char*)workspace;
     a.drow = (float*)w;
-    a.dq_acc = dtype == FA_BF16 ? (float*)(w + align_up((size_t)bh * n_q * sizeof(float))) : nullptr;
+    a.l2pad = dtype == FA_BF16
+                  ? (float*)(w + align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * sizeof(float)))
+                  : nullptr;
     return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
 

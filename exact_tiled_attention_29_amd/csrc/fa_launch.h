@@ -35,8 +35,8 @@ struct BwdArgs {
     bool causal;
     bool o_f32;
     float scale;
-    float* dq_acc;  // fp32 [bh, n_q, d] (bf16 path only)
-    float* drow;    // fp32 [bh, n_q]: D = rowsum(dO * O)
+    float* drow;    // fp32 D = rowsum(dO * O): [bh, n_q] (fp32 path) or [bh, n_q_pad] (bf16)
+    float* l2pad;   // fp32 [bh, n_q_pad] L * log2(e), +inf on padding rows (bf16 path)
     hipEvent_t const* events;  // NULL or 4 events: before D, before dK/dV, after dK/dV, end
 };
 
@@ -45,9 +45,8 @@ inline hipError_t record_stage(const BwdArgs& a, int i, hipStream_t st) {
     return a.events ? hipEventRecord(a.events[i], st) : hipSuccess;
 }
 
-// Rows per head of the bf16 backward's fp32 dQ accumulator: n_q rounded up
-// to the 32-row query tile, so the dK/dV kernel's atomic adds need no row
-// guard (the padding rows are scratch and never read back).
+// Rows per head of the bf16 backward's L2 and D arrays: n_q rounded up to the
+// 32-row query tile of the dK/dV kernel, so whole tiles can be copied.
 inline int dq_rows_padded(int n_q) { return (n_q + 31) / 32 * 32; }
 
 // bf16 path (MFMA).

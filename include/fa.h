@@ -75,9 +75,9 @@ int fa_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (0 for an empty
- * call). bf16: the fp32 row term D [B,H,n_q] plus an fp32 dQ accumulator
- * [B,H,ceil(n_q/32)*32,d] (each 256-byte aligned); float32: D only.
- * Returns 0 for arguments fa_bwd would reject.
+ * call). bf16: the fp32 row term D and L * log2(e), each [B,H,ceil(n_q/32)*32]
+ * and 256-byte aligned; float32: D [B,H,n_q]. Returns 0 for arguments
+ * fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
                               int dtype, int causal);
@@ -99,8 +99,7 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
  * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
  * 256-byte aligned, owned by the caller, contents on entry ignored. Calls
  * that overlap in time must not share a workspace.
- * bf16 dQ is accumulated with fp32 atomics, so its last bits may vary from
- * run to run; dK, dV and the float32 path are deterministic.
+ * Results are deterministic: the same inputs give bitwise the same outputs.
  */
 int fa_bwd(const void* q, const void* k, const void* v,
            const void* o, int o_dtype, const float* lse, const void* d_o,
@@ -113,9 +112,9 @@ int fa_bwd(const void* q, const void* k, const void* v,
  * fa_bwd with per-kernel timing: identical arguments and results, plus
  * `events`, NULL or an array of 4 hipEvent_t (passed as void*) created by
  * the caller with timing enabled. They are recorded on `stream` before the
- * row-term kernel (D = rowsum(dO * O)), before the dK/dV kernel, after it,
- * and after the last kernel, so hipEventElapsedTime gives each stage's
- * duration. For the callers that need the dominant kernel's own time (the
+ * row-term kernel (D = rowsum(dO * O)), before the dK/dV kernel, after it
+ * (= before the dQ kernel), and after the dQ kernel, so hipEventElapsedTime
+ * gives each stage's duration. Not recorded for an empty call. For the callers that need the dominant kernel's own time (the
  * benchmark); the computation is the one fa_bwd documents.
  */
 int fa_bwd_timed(const void* q, const void* k, const void* v,
