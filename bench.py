@@ -13,7 +13,8 @@ the timed region) and the fp64 CPU oracle timed on a bounded sample of the
 same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
-  python bench.py --summarize-pmc DIR      # HBM bytes from rocprofv3 --pmc runs
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --summary-out F   # HBM bytes per kernel
+  python bench.py --summarize-stats DIR --summary-out F                  # kernel durations
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # 256 CUs x 4096 FLOP/clk x 2.4 GHz = 2516.6
 METRIC = "attention TFLOP/s fwd+bwd (bf16, causal, n=4096, d=128); % MFMA peak"
 CSRC = os.path.join(ROOT, "exact_tiled_attention_29_amd", "csrc")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_dkdv_self_b2h32_n4096_d128_causal_pmc.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_self_b2h32_n4096_d128_causal.txt")
 
 
 def kernel_source_hash() -> str:
@@ -58,7 +59,7 @@ def _read_counter_csv(d):
     return rows
 
 
-def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_path):
+def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_path, command=""):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each kernel, scaled by
     what the counters read for a plain copy kernel of copy_bytes bytes."""
     def per_kernel(d, counter):
@@ -75,12 +76,30 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_path):
     copy_w = [v for k, v in write.items() if "copy" in k.lower() or "elementwise" in k.lower()]
     fs = copy_bytes / (max(copy_f) * 1024) if copy_f else 1.0
     ws = copy_bytes / (max(copy_w) * 1024) if copy_w else 1.0
-    lines = [f"source_hash {kernel_source_hash()}",
+    lines = [f"command: {command}", f"source_hash {kernel_source_hash()}",
              f"copy_bytes {copy_bytes} fetch_scale {fs:.4f} write_scale {ws:.4f}"]
     for k in sorted(set(fetch) | set(write)):
         f_ = fetch.get(k, float("nan")) * 1024 * fs
         w_ = write.get(k, float("nan")) * 1024 * ws
         lines.append(f"kernel {k[:120]!r} fetch_bytes {f_:.0f} write_bytes {w_:.0f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_stats(stats_dir, out_path, command):
+    """Per-kernel call count and average duration from rocprofv3 --stats."""
+    import csv
+    rows = []
+    for f in glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    lines = [f"command: {command}", f"source_hash {kernel_source_hash()}",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):6.2f}")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -139,18 +158,23 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads the oracle baseline runs")
+    ap.add_argument("--cpu-heads", type=int, default=10, help="heads the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summary-out", default=PMC_SUMMARY)
     ap.add_argument("--summary-copy-mib", type=int, default=512)
+    ap.add_argument("--summary-command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summary_copy_mib << 20,
-                      args.summary_out)
+                      args.summary_out, args.summary_command)
+        return 0
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.summary_out, args.summary_command)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
