@@ -133,8 +133,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = zero_f32x16();
 
-    // Copy query tile t (rows q0 .. q0+31; rows past n_q read row n_q - 1, whose
-    // L2 = +inf padding makes their P = 0) and its L2, D values into LDS.
+    // Copy query tile t (rows q0 .. q0+31; rows past n_q fall outside the
+    // buffer and read as zeros, and their L2 = +inf padding makes P = 0) and
+    // its L2, D values into LDS.
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, n_q * D * 2);
+    const __amdgpu_buffer_rsrc_t dors = make_rsrc(dOh, n_q * D * 2);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(l2h, n_q_pad * 4);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dph, n_q_pad * 4);
     auto issue_tile = [&](bf16* Qd, bf16* dOd, float* LDd, int t) {
         const int q0 = t * kBQ;
 #pragma unroll
@@ -143,30 +148,41 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
             const int p = 64 * b + lane;
             const int row = p / (D / 8), pc = p % (D / 8);
             const int chunk = pc ^ tile_swz<D>(row);
-            const int goff = min(q0 + row, n_q - 1) * D + 8 * chunk;
-            load_lds16(Qh + goff, Qd + 512 * b);
-            load_lds16(dOh + goff, dOd + 512 * b);
+            const int boff = ((q0 + row) * D + 8 * chunk) * 2;
+            load_lds16(qrs, boff, Qd + 512 * b);
+            load_lds16(dors, boff, dOd + 512 * b);
         }
-        if (wave == 0 && lane < 16)   // 8 lanes x 16 B of L2, then 8 of D (q0 is a multiple of 32 < n_q_pad)
-            load_lds16((lane < 8 ? l2h + q0 + 4 * lane : dph + q0 + 4 * (lane - 8)), LDd);
+        // 8 lanes x 16 B of L2, then 8 of D (q0 is a multiple of 32 < n_q_pad)
+        if (wave == 0 && lane < 16)
+            load_lds16(lane < 8 ? lrs : drs, (q0 + 4 * (lane & 7)) * 4, LDd);
     };
 
     // S, dP, P, dS, dV, dK for one staged query tile.
     auto tile_step = [&](const bf16* Qb, const bf16* dOb, const float* LDb, int q0) {
         const bool active = kw0 < n_k && (!CAUSAL || q0 + kBQ - 1 >= kw0);
         if (!active) return;
-        // S = Q K^T and dP = dO V^T (rows = queries, columns = keys).
+        // S = Q K^T and dP = dO V^T (rows = queries, columns = keys); the Q
+        // and dO operands are read one k-step ahead of their MFMAs.
         f32x16 s = zero_f32x16(), dpv = zero_f32x16();
+        bf16x8 aq[2], ad[2];
+        aq[0] = *(const bf16x8*)(&Qb[tile_off<D>(r, 8 * g)]);
+        ad[0] = *(const bf16x8*)(&dOb[tile_off<D>(r, 8 * g)]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 aq = *(const bf16x8*)(&Qb[tile_off<D>(r, 16 * kk + 8 * g)]);
-            const bf16x8 ad = *(const bf16x8*)(&dOb[tile_off<D>(r, 16 * kk + 8 * g)]);
-            s = mfma32(aq, kreg[kk], s);
-            dpv = mfma32(ad, vreg[kk], dpv);
+            if (kk + 1 < KK) {
+                aq[(kk + 1) & 1] = *(const bf16x8*)(&Qb[tile_off<D>(r, 16 * (kk + 1) + 8 * g)]);
+                ad[(kk + 1) & 1] = *(const bf16x8*)(&dOb[tile_off<D>(r, 16 * (kk + 1) + 8 * g)]);
+            }
+            s = mfma32(aq[kk & 1], kreg[kk], s);
+            dpv = mfma32(ad[kk & 1], vreg[kk], dpv);
         }
-        // Lane holds key kw0 + r; element v is query q0 + acc_row(v, g).
+        sched_reads_ahead_of_mfma<KK>();
+        // Lane holds key kw0 + r; element v is query q0 + 4g + 8*(v/4) + v%4.
+        // Masked (keys past n_k; causal: key after the query) iff the
+        // constant 8*(v/4) + v%4 is below a per-lane limit.
         const int key = kw0 + r;
         const bool need_mask = (kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0);
+        const int lim = key >= n_k ? 64 : (CAUSAL ? key - q0 - 4 * g : -1);
         bf16x8 pa[2], dsa[2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
             for (int j = 0; j < 4; ++j) {
                 const int v = 4 * i + j;
                 float p = fast_exp2(fmaf(s[v], scale2, -lq[j]));
-                if (need_mask && (key >= n_k || (CAUSAL && key > q0 + acc_row(v, g)))) p = 0.0f;
+                if (need_mask && 8 * i + j < lim) p = 0.0f;
                 const float ds = p * (dpv[v] - dq[j]);
                 pa[v >> 3][v & 7] = to_bf16(p);
                 dsa[v >> 3][v & 7] = to_bf16(ds);
@@ -289,6 +305,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     if (CAUSAL) kend = min(n_k, min(q0 + BR, n_q));
     const int ntiles = (kend + kBC - 1) / kBC;
 
+    // K, V tiles straight to LDS; rows past n_k read as zeros (masked keys).
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kh, n_k * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vh, n_k * D * 2);
     auto issue_tile = [&](bf16* Kd, bf16* Vd, int ks) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
@@ -296,9 +315,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             const int p = 64 * b + lane;
             const int rw = p / (D / 8), pc = p % (D / 8);
             const int chunk = pc ^ tile_swz<D>(rw);
-            const int goff = min(ks + rw, n_k - 1) * D + 8 * chunk;
-            load_lds16(Kh + goff, Kd + 512 * b);
-            load_lds16(Vh + goff, Vd + 512 * b);
+            const int boff = ((ks + rw) * D + 8 * chunk) * 2;
+            load_lds16(krs, boff, Kd + 512 * b);
+            load_lds16(vrs, boff, Vd + 512 * b);
         }
     };
 
@@ -314,23 +333,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         // Two 32-key halves, one after the other, to keep fewer values live.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            // S^T = K Q^T and dP^T = V dO^T (rows = keys, columns = queries).
+            // S^T = K Q^T and dP^T = V dO^T (rows = keys, columns = queries);
+            // K and V operands are read one k-step ahead of their MFMAs.
             f32x16 s = zero_f32x16(), dpt = zero_f32x16();
+            bf16x8 ak[2], av[2];
+            ak[0] = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 8 * g)]);
+            av[0] = *(const bf16x8*)(&Vb[tile_off<D>(32 * kb + r, 8 * g)]);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const bf16x8 ak = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 16 * kk + 8 * g)]);
-                const bf16x8 av = *(const bf16x8*)(&Vb[tile_off<D>(32 * kb + r, 16 * kk + 8 * g)]);
-                s = mfma32(ak, qreg[kk], s);
-                dpt = mfma32(av, doreg[kk], dpt);
+                if (kk + 1 < KK) {
+                    ak[(kk + 1) & 1] = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 16 * (kk + 1) + 8 * g)]);
+                    av[(kk + 1) & 1] = *(const bf16x8*)(&Vb[tile_off<D>(32 * kb + r, 16 * (kk + 1) + 8 * g)]);
+                }
+                s = mfma32(ak[kk & 1], qreg[kk], s);
+                dpt = mfma32(av[kk & 1], doreg[kk], dpt);
             }
+            sched_reads_ahead_of_mfma<KK>();
+            // key of element v: ks + 32kb + 4g + 8*(v/4) + v%4 (see the forward)
+            const int lim = (CAUSAL ? min(n_k, row + 1) : n_k) - ks - 32 * kb - 4 * g;
             bf16x8 dsb[2];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 float p = fast_exp2(fmaf(s[v], scale2, -l2));
-                if (need_mask) {
-                    const int key = ks + 32 * kb + acc_row(v, g);
-                    if (key >= n_k || (CAUSAL && key > row)) p = 0.0f;
-                }
+                if (need_mask && 8 * (v >> 2) + (v & 3) >= lim) p = 0.0f;
                 dsb[v >> 3][v & 7] = to_bf16(p * (dpt[v] - drw));
             }
             // dQ^T (d x queries) += K^T dS^T; K^T operands by transpose reads.

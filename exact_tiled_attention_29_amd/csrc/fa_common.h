@@ -118,10 +118,33 @@ __device__ __forceinline__ int tile_off(int row, int col) {
     return row * D + 8 * ((col >> 3) ^ tile_swz<D>(row)) + (col & 7);
 }
 
-// 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4):
-// lane l's 16 bytes land at lds_base + 16*l; lds_base must be wave-uniform.
-__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+// Scheduling hint for an unrolled loop of STEPS steps, each with 2 LDS reads
+// (for the next step) and 2 MFMAs: keep the reads one step ahead of the
+// MFMAs that consume them instead of clustering or serialising them.
+template <int STEPS>
+__device__ __forceinline__ void sched_reads_ahead_of_mfma() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads of steps 0 and 1
+#pragma unroll
+    for (int i = 0; i < STEPS - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs of step i
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads of step i + 2
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMAs of the last two steps
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw, 32-bit data format):
+// buffer loads at byte offsets >= bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16-byte global -> LDS copy that bypasses registers (buffer_load_dwordx4 ...
+// lds): lane l's 16 bytes, read at byte offset `voff` of the resource, land at
+// lds_base + 16*l; lds_base must be wave-uniform. A buffer (not a flat/global)
+// load, so the compiler keeps precise waits on the LDS reads that follow.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, int voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds_base),
+                                             16, voff, 0, 0, 0);
 }
 
 // Map a hardware workgroup index to a logical one so that each of the 8

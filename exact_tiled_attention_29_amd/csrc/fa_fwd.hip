@@ -86,7 +86,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // K and V tiles go straight from global memory to LDS (no registers),
     // row-major with swizzled 16-byte chunks. Each wave copies LPW blocks of
     // 1 KB: lane l of block b fills chunk position 64*b + l. Rows past n_k
-    // read row n_k - 1 (finite data; those keys are masked).
+    // fall outside the buffer resource and read as zeros (those keys are
+    // masked).
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kh, n_k * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vh, n_k * D * 2);
     auto issue_tile = [&](bf16* Kd, bf16* Vd, int ks) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
@@ -94,9 +97,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             const int p = 64 * b + lane;
             const int row = p / (D / 8), pc = p % (D / 8);
             const int chunk = pc ^ tile_swz<D>(row);
-            const int goff = min(ks + row, n_k - 1) * D + 8 * chunk;
-            load_lds16(Kh + goff, Kd + 512 * b);
-            load_lds16(Vh + goff, Vd + 512 * b);
+            const int boff = ((ks + row) * D + 8 * chunk) * 2;
+            load_lds16(krs, boff, Kd + 512 * b);
+            load_lds16(vrs, boff, Vd + 512 * b);
         }
     };
 
@@ -111,28 +114,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     auto tile_step = [&](const bf16* Kb, const bf16* Vb, int ks) {
         const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row);
         if (active) {
-            // S^T (keys x queries) for two 32-key blocks.
+            // S^T (keys x queries) for two 32-key blocks. K operands are read
+            // one k-step ahead, so each step's LDS reads overlap the previous
+            // step's MFMAs.
             f32x16 s[2];
             s[0] = s[1] = zero_f32x16();
+            bf16x8 ka[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                ka[0][kb] = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 8 * g)]);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
+                if (kk + 1 < KK) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 a = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 16 * kk + 8 * g)]);
-                    s[kb] = mfma32(a, qreg[kk], s[kb]);
+                    for (int kb = 0; kb < 2; ++kb)
+                        ka[(kk + 1) & 1][kb] =
+                            *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 16 * (kk + 1) + 8 * g)]);
                 }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[kk & 1][kb], qreg[kk], s[kb]);
             }
-            // Mask: keys past n_k, and (causal) keys after the query.
+            sched_reads_ahead_of_mfma<KK>();
+            // Mask keys past n_k and (causal) keys after the query: the key of
+            // element v is ks + 32*kb + 4g + 8*(v/4) + v%4, so one compare of a
+            // constant against a per-lane limit decides it.
             const bool need_mask = (ks + kBC > n_k) || (CAUSAL && ks + kBC - 1 > qw);
             if (need_mask) {
-                const int row = qw + r;
+                const int lim = (CAUSAL ? min(n_k, qw + r + 1) : n_k) - ks - 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = ks + 32 * kb + acc_row(v, g);
-                        if (key >= n_k || (CAUSAL && key > row)) s[kb][v] = kNegInf;
-                    }
+                    for (int v = 0; v < 16; ++v)
+                        if (32 * kb + 8 * (v >> 2) + (v & 3) >= lim) s[kb][v] = kNegInf;
             }
             // Online softmax in the exp2 domain against a reference max m_ref
             // that only moves when the row max exceeds it by more than 2^kTau;
