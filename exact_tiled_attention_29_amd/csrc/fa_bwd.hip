@@ -222,16 +222,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     const int t_begin = CAUSAL ? k0 / kBQ : 0;
     if (t_begin < nqt) {
         issue_tile(Qs0, dOs0, LD0, t_begin);
-        __syncthreads();
+        copies_barrier();
         // Unrolled by two so each step names its buffers at compile time.
         for (int t = t_begin; t < nqt; t += 2) {
             if (t + 1 < nqt) issue_tile(Qs1, dOs1, LD1, t + 1);
             tile_step(Qs0, dOs0, LD0, t * kBQ);
-            __syncthreads();  // tile t+1 landed; tile t reads done
+            copies_barrier();  // tile t+1 landed; tile t reads done
             if (t + 1 >= nqt) break;
             if (t + 2 < nqt) issue_tile(Qs0, dOs0, LD0, t + 2);
             tile_step(Qs1, dOs1, LD1, (t + 1) * kBQ);
-            __syncthreads();
+            copies_barrier();
         }
     }
 
@@ -373,15 +373,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     };
 
     issue_tile(Ks0, Vs0, 0);
-    __syncthreads();
+    copies_barrier();
     for (int t = 0; t < ntiles; t += 2) {
         if (t + 1 < ntiles) issue_tile(Ks1, Vs1, (t + 1) * kBC);
         tile_step(Ks0, Vs0, t * kBC);
-        __syncthreads();
+        copies_barrier();
         if (t + 1 >= ntiles) break;
         if (t + 2 < ntiles) issue_tile(Ks0, Vs0, (t + 2) * kBC);
         tile_step(Ks1, Vs1, (t + 1) * kBC);
-        __syncthreads();
+        copies_barrier();
     }
 
     if (row < n_q) {

@@ -80,6 +80,14 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Workgroup barrier after direct global -> LDS copies: each wave first waits
+// for its own copies (vmcnt) and LDS writes (lgkmcnt), so after the barrier
+// every wave sees every wave's data. Written out because the compiler orders
+// a wave's copy only against that wave's own later reads of the same buffer.
+__device__ __forceinline__ void copies_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, the lane with local index
 // 4*a + e receives element e of the 8-byte chunks addressed by the lanes
 // a, 4 + a, 8 + a, 12 + a (in that order). When lane s of the group points
@@ -136,6 +144,22 @@ __device__ __forceinline__ void sched_reads_ahead_of_mfma() {
 // buffer loads at byte offsets >= bytes return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Scheduling hint for the pipelined step "S^T of the next tile under the
+// softmax of this one": KK k-steps of 2 LDS reads + 2 MFMAs, with the
+// softmax's VALU work spread between the MFMAs.
+template <int KK>
+__device__ __forceinline__ void sched_scores_under_softmax() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);      // K reads of k-steps 0, 1
+#pragma unroll
+    for (int i = 0; i < KK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);  // VALU
+        if (i + 2 < KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // reads of step i + 2
+    }
 }
 
 // 16-byte global -> LDS copy that bypasses registers (buffer_load_dwordx4 ...

@@ -194,16 +194,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     };
 
     issue_tile(Ks0, Vs0, 0);
-    __syncthreads();
+    copies_barrier();
     // Unrolled by two so each step names its buffers at compile time.
     for (int t = 0; t < ntiles; t += 2) {
         if (t + 1 < ntiles) issue_tile(Ks1, Vs1, (t + 1) * kBC);
         tile_step(Ks0, Vs0, t * kBC);
-        __syncthreads();  // tile t+1 landed (each wave waited for its copies); tile t reads done
+        copies_barrier();  // tile t+1 landed (each wave waited for its copies); tile t reads done
         if (t + 1 >= ntiles) break;
         if (t + 2 < ntiles) issue_tile(Ks0, Vs0, (t + 2) * kBC);
         tile_step(Ks1, Vs1, (t + 1) * kBC);
-        __syncthreads();
+        copies_barrier();
     }
 
     // Epilogue: O / l, L = ln 2 * (m + log2 l).
