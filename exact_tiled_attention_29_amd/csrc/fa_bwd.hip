@@ -102,9 +102,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
 
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int bh = logical / n_ktiles;
-    const int kt = logical % n_ktiles;   // ascending: longest causal work first
+    int bh, kt;   // rank = key tile, ascending: longest causal work first
+    work_item(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, &bh, &kt);
     const int k0 = kt * BKV;
     const int kw0 = k0 + 32 * wave;      // this wave's first key
 
@@ -273,9 +272,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
 
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int bh = logical / n_qtiles;
-    const int qt = n_qtiles - 1 - logical % n_qtiles;
+    int bh, rank;   // rank 0 = last query tile: longest causal work first
+    work_item(blockIdx.x, gridDim.x / n_qtiles, n_qtiles, &bh, &rank);
+    const int qt = n_qtiles - 1 - rank;
     const int q0 = qt * BR;
     const int qw = q0 + wave * RW;
 

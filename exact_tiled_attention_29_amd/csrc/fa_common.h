@@ -171,13 +171,25 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, int voff
                                              16, voff, 0, 0, 0);
 }
 
-// Map a hardware workgroup index to a logical one so that each of the 8
-// XCDs (which receive workgroups round-robin: id % 8) works through one
-// contiguous range of logical ids. Bijective for any n.
-__device__ __forceinline__ int xcd_logical_id(int bid, int n) {
-    const int q = n >> 3, rem = n & 7;
-    const int xcd = bid & 7, slot = bid >> 3;
-    return xcd < rem ? xcd * (q + 1) + slot : rem * (q + 1) + (xcd - rem) * q + slot;
+// Work order of a grid of n_bh * n_tiles workgroups (one per (head, tile)).
+// Workgroups go round-robin to the 8 XCDs (id % 8). When the heads split
+// evenly over the XCDs, each XCD gets its own heads (their K/V re-reads stay
+// in that XCD's L2) and runs its work by rank: rank 0 first for all its heads,
+// then rank 1, and so on, so the longest causal tiles (rank 0) start first and
+// the short ones fill the end. Otherwise ranks are interleaved over all
+// heads. Returns the head in *bh and the rank in *rank.
+__device__ __forceinline__ void work_item(int bid, int n_bh, int n_tiles, int* bh, int* rank) {
+    const int n = n_bh * n_tiles;
+    if ((n_bh & 7) == 0) {
+        const int hpx = n_bh >> 3;                 // heads per XCD
+        const int xcd = bid & 7, slot = bid >> 3;  // slot < hpx * n_tiles
+        *bh = xcd * hpx + slot % hpx;
+        *rank = slot / hpx;
+    } else {
+        const int l = bid < n ? bid : n - 1;
+        *bh = l % n_bh;
+        *rank = l / n_bh;
+    }
 }
 
 }  // namespace fa

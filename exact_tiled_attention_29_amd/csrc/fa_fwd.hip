@@ -57,9 +57,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
 
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int bh = logical / n_qtiles;
-    const int qt = n_qtiles - 1 - logical % n_qtiles;
+    int bh, rank;   // rank 0 = last query tile: longest causal work first
+    work_item(blockIdx.x, gridDim.x / n_qtiles, n_qtiles, &bh, &rank);
+    const int qt = n_qtiles - 1 - rank;
     const int q0 = qt * BR;
     const int qw = q0 + wave * RW;
 

@@ -167,14 +167,18 @@ def test_empty_calls():
     assert (dk == 0).all() and (dv == 0).all()
 
 
-def test_forward_is_deterministic():
-    w = workloads.custom(2, 4, 640, 640, 128, "bf16", True)
+@pytest.mark.parametrize("d,causal,n", [(128, True, 2048), (64, False, 1024), (128, False, 1536)])
+def test_forward_is_deterministic(d, causal, n):
+    # Repeated runs are bitwise equal (tiles are staged and consumed under
+    # barriers; a tile read before every wave's copy lands shows up here).
+    w = workloads.custom(2, 8, n, n, d, "bf16", causal)
     q, k, v, _ = make_inputs(w, seed=1)
     qg, kg, vg = (t.cuda() for t in (q, k, v))
-    o1, l1 = fa.forward(qg, kg, vg, True)
-    o2, l2 = fa.forward(qg, kg, vg, True)
-    torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o1, l1 = fa.forward(qg, kg, vg, causal)
+    for _ in range(3):
+        o2, l2 = fa.forward(qg, kg, vg, causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("causal", [False, True])
