@@ -160,6 +160,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     auto tile_step = [&](const bf16* Qb, const bf16* dOb, const float* LDb, int q0) {
         const bool active = kw0 < n_k && (!CAUSAL || q0 + kBQ - 1 >= kw0);
         if (!active) return;
+        mfma_priority(true);
         // S = Q K^T and dP = dO V^T (rows = queries, columns = keys); the Q
         // and dO operands are read one k-step ahead of their MFMAs.
         f32x16 s = zero_f32x16(), dpv = zero_f32x16();
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
             dpv = mfma32(ad[kk & 1], vreg[kk], dpv);
         }
         sched_reads_ahead_of_mfma<KK>();
+        mfma_priority(false);
         // Lane holds key kw0 + r; element v is query q0 + 4g + 8*(v/4) + v%4.
         // Masked (keys past n_k; causal: key after the query) iff the
         // constant 8*(v/4) + v%4 is below a per-lane limit.
@@ -202,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
         // dV += P^T dO, dK += dS^T Q (rows = keys, columns = d). The B
         // operands carry queries 16c + 8*(e/4) + 4g + e%4 in slot (g, e),
         // matching the accumulator order of P and dS.
+        mfma_priority(true);
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -215,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
                 dv[db] = mfma32(pa[c], bdo, dv[db]);
                 dk[db] = mfma32(dsa[c], bq, dk[db]);
             }
+        mfma_priority(false);
     };
 
     const int nqt = (n_q + kBQ - 1) / kBQ;
@@ -332,6 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         // Two 32-key halves, one after the other, to keep fewer values live.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            mfma_priority(true);
             // S^T = K Q^T and dP^T = V dO^T (rows = keys, columns = queries);
             // K and V operands are read one k-step ahead of their MFMAs.
             f32x16 s = zero_f32x16(), dpt = zero_f32x16();
@@ -348,6 +353,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 dpt = mfma32(av[kk & 1], doreg[kk], dpt);
             }
             sched_reads_ahead_of_mfma<KK>();
+            mfma_priority(false);
             // key of element v: ks + 32kb + 4g + 8*(v/4) + v%4 (see the forward)
             const int lim = (CAUSAL ? min(n_k, row + 1) : n_k) - ks - 32 * kb - 4 * g;
             bf16x8 dsb[2];
@@ -358,6 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 dsb[v >> 3][v & 7] = to_bf16(p * (dpt[v] - drw));
             }
             // dQ^T (d x queries) += K^T dS^T; K^T operands by transpose reads.
+            mfma_priority(true);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -368,6 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                                             lds_read_tr(&Kb[tile_off<D>(row0 + 8, col)]));
                     acc[db] = mfma32(a, dsb[c], acc[db]);
                 }
+            mfma_priority(false);
         }
     };
 

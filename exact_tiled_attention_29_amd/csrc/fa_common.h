@@ -73,6 +73,14 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
     return z;
 }
 
+// Issue priority of this wave on its SIMD: raised around blocks of MFMAs so
+// they issue as soon as the matrix core is free, while the other wave on
+// the SIMD fills the gaps with its VALU work.
+__device__ __forceinline__ void mfma_priority(bool high) {
+    if (high) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // Workgroup barrier that waits only for this wave's LDS operations: global
 // loads and atomics still in flight are not waited for (a __syncthreads()
 // would also drain every outstanding global store and atomic).
