@@ -23,6 +23,8 @@
 // no atomics and no dS round trip through memory, keeps each kernel within a
 // register budget that lets the hardware overlap waves, and makes every
 // gradient deterministic.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -75,10 +77,16 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 }
 
 // --------------------------------------------------------------------------
-// 2. dK, dV: key-stationary.
+// 2. dK, dV: key-stationary, software-pipelined.
 // --------------------------------------------------------------------------
+// One wave per SIMD (the K/V operands and dK/dV accumulators take most of
+// the register file), so the wave overlaps its own work: while the matrix
+// core computes S and dP of query tile t+1, the wave's VALU turns S, dP of
+// tile t into P and dS; then dV, dK of tile t follow. Query tiles stream
+// through a ring of three LDS buffers: t (read by the dV/dK products), t+1
+// (read by the S/dP products) and t+2 (being copied).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
     bf16* __restrict__ dK, bf16* __restrict__ dV,
@@ -93,10 +101,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     // row-major with swizzled 16-byte chunks; L2 and D of the tile's rows.
     __shared__ __attribute__((aligned(16))) bf16 Qs0[TILE];
     __shared__ __attribute__((aligned(16))) bf16 Qs1[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 Qs2[TILE];
     __shared__ __attribute__((aligned(16))) bf16 dOs0[TILE];
     __shared__ __attribute__((aligned(16))) bf16 dOs1[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 dOs2[TILE];
     __shared__ __attribute__((aligned(16))) float LD0[2 * kBQ];
     __shared__ __attribute__((aligned(16))) float LD1[2 * kBQ];
+    __shared__ __attribute__((aligned(16))) float LD2[2 * kBQ];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -106,6 +117,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     work_item(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, &bh, &kt);
     const int k0 = kt * BKV;
     const int kw0 = k0 + 32 * wave;      // this wave's first key
+    const int key = kw0 + r;             // this lane's key (column of S, dP)
 
     const bf16* Qh = Q + (size_t)bh * n_q * D;
     const bf16* dOh = dO + (size_t)bh * n_q * D;
@@ -117,7 +129,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     // K, V rows of this wave's keys as B operands (column = key, k = d).
     bf16x8 kreg[KK], vreg[KK];
     {
-        const int key = kw0 + r;
         const int kc = min(key, n_k - 1);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -151,90 +162,198 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
             load_lds16(qrs, boff, Qd + 512 * b);
             load_lds16(dors, boff, dOd + 512 * b);
         }
-        // 8 lanes x 16 B of L2, then 8 of D (q0 is a multiple of 32 < n_q_pad)
-        if (wave == 0 && lane < 16)
-            load_lds16(lane < 8 ? lrs : drs, (q0 + 4 * (lane & 7)) * 4, LDd);
+        // lanes 0-7: 8 x 16 B of L2 into LDd[0..31]; lanes 8-15: D into
+        // LDd[32..63] (q0 is a multiple of 32 < n_q_pad)
+        if (wave == 0) {
+            if (lane < 8) load_lds16(lrs, (q0 + 4 * lane) * 4, LDd);
+            else if (lane < 16) load_lds16(drs, (q0 + 4 * (lane - 8)) * 4, LDd);
+        }
     };
 
-    // S, dP, P, dS, dV, dK for one staged query tile.
-    auto tile_step = [&](const bf16* Qb, const bf16* dOb, const float* LDb, int q0) {
-        const bool active = kw0 < n_k && (!CAUSAL || q0 + kBQ - 1 >= kw0);
-        if (!active) return;
-        mfma_priority(true);
-        // S = Q K^T and dP = dO V^T (rows = queries, columns = keys); the Q
-        // and dO operands are read one k-step ahead of their MFMAs.
-        f32x16 s = zero_f32x16(), dpv = zero_f32x16();
-        bf16x8 aq[2], ad[2];
-        aq[0] = *(const bf16x8*)(&Qb[tile_off<D>(r, 8 * g)]);
-        ad[0] = *(const bf16x8*)(&dOb[tile_off<D>(r, 8 * g)]);
+    // Per-lane element offsets of the LDS operand reads, the same for every
+    // buffer. Each step passes them through an empty asm so that the
+    // buffer's base is added inside the step and folds into the read's
+    // immediate offset (otherwise every buffer/offset pair is hoisted out of
+    // the loop into a register of its own).
+    //  soff[kk]:       Q / dO row r, k-step kk (A operands of S and dP);
+    //  troff[c][j][h]: transpose reads for dV / dK, B operand of product
+    //                  (c, db = j), rows 16c + 4g + s16/4 + 8h.
+    int soff[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) soff[kk] = tile_off<D>(r, 16 * kk + 8 * g);
+    int troff[2][NDB][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                troff[c][db][h] = tile_off<D>(16 * c + 4 * g + (s16 >> 2) + 8 * h,
+                                              32 * db + 16 * half + 4 * (s16 & 3));
+    auto launder_offsets = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(troff[c][db][h]));
+    };
+
+    // S = Q K^T and dP = dO V^T of one staged tile (rows = queries, columns
+    // = keys). Lane holds key kw0 + r; element v is query q0 + acc_row(v, g).
+    // The Q, dO operands are read two k-steps ahead of their MFMAs.
+    auto scores = [&](const bf16* Qb, const bf16* dOb, f32x16& s, f32x16& dpv) {
+        s = zero_f32x16();
+        dpv = zero_f32x16();
+        bf16x8 aq[3], ad[3];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            aq[kk] = *(const bf16x8*)(&Qb[soff[kk]]);
+            ad[kk] = *(const bf16x8*)(&dOb[soff[kk]]);
+        }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 1 < KK) {
-                aq[(kk + 1) & 1] = *(const bf16x8*)(&Qb[tile_off<D>(r, 16 * (kk + 1) + 8 * g)]);
-                ad[(kk + 1) & 1] = *(const bf16x8*)(&dOb[tile_off<D>(r, 16 * (kk + 1) + 8 * g)]);
+            if (kk + 2 < KK) {
+                aq[(kk + 2) % 3] = *(const bf16x8*)(&Qb[soff[kk + 2]]);
+                ad[(kk + 2) % 3] = *(const bf16x8*)(&dOb[soff[kk + 2]]);
             }
-            s = mfma32(aq[kk & 1], kreg[kk], s);
-            dpv = mfma32(ad[kk & 1], vreg[kk], dpv);
+            s = mfma32(aq[kk % 3], kreg[kk], s);
+            dpv = mfma32(ad[kk % 3], vreg[kk], dpv);
         }
-        sched_reads_ahead_of_mfma<KK>();
-        mfma_priority(false);
-        // Lane holds key kw0 + r; element v is query q0 + 4g + 8*(v/4) + v%4.
-        // Masked (keys past n_k; causal: key after the query) iff the
-        // constant 8*(v/4) + v%4 is below a per-lane limit.
-        const int key = kw0 + r;
-        const bool need_mask = (kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0);
-        const int lim = key >= n_k ? 64 : (CAUSAL ? key - q0 - 4 * g : -1);
-        bf16x8 pa[2], dsa[2];
+    };
+
+    // L2 and D of the 16 queries this lane's accumulator elements hold:
+    // element v = 4i + j is query q0 + 8i + 4g + j.
+    auto read_ld = [&](const float* LDb, float* lq, float* dq) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float4 l4 = *(const float4*)(&LDb[8 * i + 4 * g]);
             const float4 d4 = *(const float4*)(&LDb[kBQ + 8 * i + 4 * g]);
-            const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
+            lq[4 * i] = l4.x; lq[4 * i + 1] = l4.y; lq[4 * i + 2] = l4.z; lq[4 * i + 3] = l4.w;
+            dq[4 * i] = d4.x; dq[4 * i + 1] = d4.y; dq[4 * i + 2] = d4.z; dq[4 * i + 3] = d4.w;
+        }
+    };
+
+    // Element v of P = exp2(S * scale * log2(e) - L2) and dS = P * (dP - D)
+    // into the bf16 A operands of the dV, dK products (k = query). MASK:
+    // zero P where the key is past n_k or (causal) after the query; the
+    // element's query offset 8*(v/4) + v%4 is masked iff it is below lim.
+    auto softmax_elem = [&](auto mask, int v, const f32x16& s, const f32x16& dpv,
+                            const float* lq, const float* dq, int lim, bf16x8* pa, bf16x8* dsa) {
+        float p = fast_exp2(fmaf(s[v], scale2, -lq[v]));
+        if (decltype(mask)::value && 8 * (v >> 2) + (v & 3) < lim) p = 0.0f;
+        pa[v >> 3][v & 7] = to_bf16(p);
+        dsa[v >> 3][v & 7] = to_bf16(p * (dpv[v] - dq[v]));
+    };
+
+    // dV += P^T dO, dK += dS^T Q of one tile (rows = keys, columns = d) from
+    // its P, dS operands; the B operands carry queries 16c + 8*(e/4) + 4g +
+    // e%4 in slot (g, e), matching the accumulator order of P and dS, and
+    // are read two products ahead. When `mask` is given, the softmax of the
+    // next tile (s, dpv -> pa_n, dsa_n) is computed between the MFMAs, EPM
+    // elements after each.
+    constexpr int NJ = 2 * NDB;                // (c, db) products of dV and of dK
+    constexpr int EPM = 16 / (2 * NJ);         // softmax elements per MFMA
+    auto grads = [&](auto with_softmax, auto mask, const bf16* Qb, const bf16* dOb,
+                     const bf16x8* pa, const bf16x8* dsa, const f32x16& s, const f32x16& dpv,
+                     const float* lq, const float* dq, int lim, bf16x8* pa_n, bf16x8* dsa_n) {
+        bf16x8 bdo[3], bq[3];
+        auto load = [&](int j, int slot) {
+            const int c = j / NDB, db = j % NDB;
+            bdo[slot] = concat(lds_read_tr(&dOb[troff[c][db][0]]), lds_read_tr(&dOb[troff[c][db][1]]));
+            bq[slot] = concat(lds_read_tr(&Qb[troff[c][db][0]]), lds_read_tr(&Qb[troff[c][db][1]]));
+        };
+        load(0, 0);
+        load(1, 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int v = 4 * i + j;
-                float p = fast_exp2(fmaf(s[v], scale2, -lq[j]));
-                if (need_mask && 8 * i + j < lim) p = 0.0f;
-                const float ds = p * (dpv[v] - dq[j]);
-                pa[v >> 3][v & 7] = to_bf16(p);
-                dsa[v >> 3][v & 7] = to_bf16(ds);
+        for (int j = 0; j < NJ; ++j) {
+            const int c = j / NDB, db = j % NDB;
+            if (j + 2 < NJ) load(j + 2, (j + 2) % 3);
+            dv[db] = mfma32(pa[c], bdo[j % 3], dv[db]);
+            if constexpr (decltype(with_softmax)::value) {
+#pragma unroll
+                for (int e = 0; e < EPM; ++e)
+                    softmax_elem(mask, 2 * EPM * j + e, s, dpv, lq, dq, lim, pa_n, dsa_n);
+            }
+            dk[db] = mfma32(dsa[c], bq[j % 3], dk[db]);
+            if constexpr (decltype(with_softmax)::value) {
+#pragma unroll
+                for (int e = 0; e < EPM; ++e)
+                    softmax_elem(mask, 2 * EPM * j + EPM + e, s, dpv, lq, dq, lim, pa_n, dsa_n);
             }
         }
-        // dV += P^T dO, dK += dS^T Q (rows = keys, columns = d). The B
-        // operands carry queries 16c + 8*(e/4) + 4g + e%4 in slot (g, e),
-        // matching the accumulator order of P and dS.
-        mfma_priority(true);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int col = 32 * db + 16 * half + 4 * (s16 & 3);
-                const int row0 = 16 * c + 4 * g + (s16 >> 2);
-                const bf16x8 bdo = concat(lds_read_tr(&dOb[tile_off<D>(row0, col)]),
-                                          lds_read_tr(&dOb[tile_off<D>(row0 + 8, col)]));
-                const bf16x8 bq = concat(lds_read_tr(&Qb[tile_off<D>(row0, col)]),
-                                         lds_read_tr(&Qb[tile_off<D>(row0 + 8, col)]));
-                dv[db] = mfma32(pa[c], bdo, dv[db]);
-                dk[db] = mfma32(dsa[c], bq, dk[db]);
-            }
-        mfma_priority(false);
     };
 
     const int nqt = (n_q + kBQ - 1) / kBQ;
     const int t_begin = CAUSAL ? k0 / kBQ : 0;
+    const std::true_type yes{};
+    const std::false_type no{};
+    auto mask_limit = [&](int q0) { return key >= n_k ? 64 : (CAUSAL ? key - q0 - 4 * g : -1); };
+    auto needs_mask = [&](int q0) { return (kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0); };
+
+    // P and dS of the previous tile (A operands of its dV, dK products).
+    bf16x8 pa_p[2], dsa_p[2];
+
+    // One step for tile t: buffers c (tile t), p (tile t-1), f (tile t+1,
+    // copied during the step). S, dP of tile t on the matrix core; then the
+    // dV, dK products of tile t-1 on the matrix core with the softmax of
+    // tile t on the VALU between them.
+    auto step = [&](bf16* Qc, bf16* dOc, float* LDc, const bf16* Qp, const bf16* dOp, bf16* Qf,
+                    bf16* dOf, float* LDf, int t) {
+        copies_barrier();  // tile t landed; every wave is done with tile t-2's buffer (f)
+        if (t + 1 < nqt) issue_tile(Qf, dOf, LDf, t + 1);
+        launder_offsets();
+        float lq[16], dq[16];
+        read_ld(LDc, lq, dq);
+        f32x16 s, dpv;
+        scores(Qc, dOc, s, dpv);
+        const int q0 = t * kBQ;
+        const int lim = mask_limit(q0);
+        bf16x8 pa[2], dsa[2];
+        if (needs_mask(q0))
+            grads(yes, yes, Qp, dOp, pa_p, dsa_p, s, dpv, lq, dq, lim, pa, dsa);
+        else
+            grads(yes, no, Qp, dOp, pa_p, dsa_p, s, dpv, lq, dq, lim, pa, dsa);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) { pa_p[c] = pa[c]; dsa_p[c] = dsa[c]; }
+    };
+
     if (t_begin < nqt) {
+        // Tile t_begin + i is staged in buffer i % 3.
         issue_tile(Qs0, dOs0, LD0, t_begin);
         copies_barrier();
-        // Unrolled by two so each step names its buffers at compile time.
-        for (int t = t_begin; t < nqt; t += 2) {
-            if (t + 1 < nqt) issue_tile(Qs1, dOs1, LD1, t + 1);
-            tile_step(Qs0, dOs0, LD0, t * kBQ);
-            copies_barrier();  // tile t+1 landed; tile t reads done
-            if (t + 1 >= nqt) break;
-            if (t + 2 < nqt) issue_tile(Qs0, dOs0, LD0, t + 2);
-            tile_step(Qs1, dOs1, LD1, (t + 1) * kBQ);
-            copies_barrier();
+        if (t_begin + 1 < nqt) issue_tile(Qs1, dOs1, LD1, t_begin + 1);
+        {
+            launder_offsets();
+            float lq[16], dq[16];
+            read_ld(LD0, lq, dq);
+            f32x16 s, dpv;
+            scores(Qs0, dOs0, s, dpv);
+            const int lim = mask_limit(t_begin * kBQ);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) softmax_elem(yes, v, s, dpv, lq, dq, lim, pa_p, dsa_p);
+        }
+        // Unrolled by three so each step names its buffers at compile time;
+        // the loop has a single exit, which keeps the dK/dV accumulators in
+        // the same registers across the steps.
+        for (int t = t_begin + 1; t < nqt; t += 3) {
+            step(Qs1, dOs1, LD1, Qs0, dOs0, Qs2, dOs2, LD2, t);
+            if (t + 1 < nqt) step(Qs2, dOs2, LD2, Qs1, dOs1, Qs0, dOs0, LD0, t + 1);
+            if (t + 2 < nqt) step(Qs0, dOs0, LD0, Qs2, dOs2, Qs1, dOs1, LD1, t + 2);
+        }
+        // dV, dK of the last tile (already staged; no copy is in flight, so
+        // its buffer may be picked at run time).
+        const int slot = (nqt - 1 - t_begin) % 3;
+        const bf16* Ql = slot == 0 ? Qs0 : (slot == 1 ? Qs1 : Qs2);
+        const bf16* dOl = slot == 0 ? dOs0 : (slot == 1 ? dOs1 : dOs2);
+        launder_offsets();
+        {
+            const f32x16 z = zero_f32x16();
+            float lz[16];
+            bf16x8 unused[2];
+            grads(no, no, Ql, dOl, pa_p, dsa_p, z, z, lz, lz, 0, unused, unused);
         }
     }
 
@@ -243,9 +362,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int key = kw0 + acc_row(v, g);
-            if (key < n_k) {
-                const size_t off = ((size_t)bh * n_k + key) * D + 32 * db + r;
+            const int kr = kw0 + acc_row(v, g);
+            if (kr < n_k) {
+                const size_t off = ((size_t)bh * n_k + kr) * D + 32 * db + r;
                 dK[off] = to_bf16(dk[db][v] * scale);
                 dV[off] = to_bf16(dv[db][v]);
             }
