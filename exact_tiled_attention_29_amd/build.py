@@ -31,6 +31,13 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source additions. The backward's MFMA results feed VALU work (the
+# softmax) right away: keep them in VGPRs (the default puts them in AGPRs
+# and copies every element back before use).
+FILE_FLAGS = {
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -45,7 +52,8 @@ def sources():
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

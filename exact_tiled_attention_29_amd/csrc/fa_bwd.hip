@@ -97,17 +97,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     constexpr int TILE = kBQ * D;      // elements per Q or dO tile
     constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KB direct copies per wave per tile
 
-    // One LDS object per buffer (see the forward kernel): Q, dO tiles
-    // row-major with swizzled 16-byte chunks; L2 and D of the tile's rows.
-    __shared__ __attribute__((aligned(16))) bf16 Qs0[TILE];
-    __shared__ __attribute__((aligned(16))) bf16 Qs1[TILE];
-    __shared__ __attribute__((aligned(16))) bf16 Qs2[TILE];
-    __shared__ __attribute__((aligned(16))) bf16 dOs0[TILE];
-    __shared__ __attribute__((aligned(16))) bf16 dOs1[TILE];
-    __shared__ __attribute__((aligned(16))) bf16 dOs2[TILE];
-    __shared__ __attribute__((aligned(16))) float LD0[2 * kBQ];
-    __shared__ __attribute__((aligned(16))) float LD1[2 * kBQ];
-    __shared__ __attribute__((aligned(16))) float LD2[2 * kBQ];
+    // One LDS object per ring slot, holding the slot's Q tile, dO tile
+    // (row-major, swizzled 16-byte chunks) and the L2, D values of its rows.
+    // Distinct objects let the compiler tell a slot being copied from slots
+    // being read (it tracks only a few copy targets, so the slot's three
+    // parts share one object).
+    constexpr int SLOT = 2 * TILE + 4 * kBQ;   // bf16 elements per slot
+    __shared__ __attribute__((aligned(16))) bf16 Sl0[SLOT];
+    __shared__ __attribute__((aligned(16))) bf16 Sl1[SLOT];
+    __shared__ __attribute__((aligned(16))) bf16 Sl2[SLOT];
+    auto q_of = [](bf16* sl) { return sl; };
+    auto do_of = [](bf16* sl) { return sl + TILE; };
+    auto ld_of = [](bf16* sl) { return (float*)(sl + 2 * TILE); };
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         }
     };
 
-    // Per-lane element offsets of the LDS operand reads, the same for every
+    // Per-lane byte offsets of the LDS operand reads, the same for every
     // buffer. Each step passes them through an empty asm so that the
     // buffer's base is added inside the step and folds into the read's
     // immediate offset (otherwise every buffer/offset pair is hoisted out of
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     //                  (c, db = j), rows 16c + 4g + s16/4 + 8h.
     int soff[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) soff[kk] = tile_off<D>(r, 16 * kk + 8 * g);
+    for (int kk = 0; kk < KK; ++kk) soff[kk] = 2 * tile_off<D>(r, 16 * kk + 8 * g);
     int troff[2][NDB][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -188,8 +189,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                troff[c][db][h] = tile_off<D>(16 * c + 4 * g + (s16 >> 2) + 8 * h,
-                                              32 * db + 16 * half + 4 * (s16 & 3));
+                troff[c][db][h] = 2 * tile_off<D>(16 * c + 4 * g + (s16 >> 2) + 8 * h,
+                                                  32 * db + 16 * half + 4 * (s16 & 3));
+    auto at = [](const bf16* base, int byte_off) {
+        return (const bf16*)((const char*)base + byte_off);
+    };
     auto launder_offsets = [&]() {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
@@ -203,24 +207,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
     // S = Q K^T and dP = dO V^T of one staged tile (rows = queries, columns
     // = keys). Lane holds key kw0 + r; element v is query q0 + acc_row(v, g).
-    // The Q, dO operands are read two k-steps ahead of their MFMAs.
+    // The Q, dO operands are read kLookS k-steps ahead of their MFMAs.
+    constexpr int kLookS = 3;
     auto scores = [&](const bf16* Qb, const bf16* dOb, f32x16& s, f32x16& dpv) {
         s = zero_f32x16();
         dpv = zero_f32x16();
-        bf16x8 aq[3], ad[3];
+        bf16x8 aq[kLookS + 1], ad[kLookS + 1];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            aq[kk] = *(const bf16x8*)(&Qb[soff[kk]]);
-            ad[kk] = *(const bf16x8*)(&dOb[soff[kk]]);
+        for (int kk = 0; kk < kLookS && kk < KK; ++kk) {
+            aq[kk] = *(const bf16x8*)at(Qb, soff[kk]);
+            ad[kk] = *(const bf16x8*)at(dOb, soff[kk]);
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 2 < KK) {
-                aq[(kk + 2) % 3] = *(const bf16x8*)(&Qb[soff[kk + 2]]);
-                ad[(kk + 2) % 3] = *(const bf16x8*)(&dOb[soff[kk + 2]]);
+            if (kk + kLookS < KK) {
+                aq[(kk + kLookS) % (kLookS + 1)] = *(const bf16x8*)at(Qb, soff[kk + kLookS]);
+                ad[(kk + kLookS) % (kLookS + 1)] = *(const bf16x8*)at(dOb, soff[kk + kLookS]);
             }
-            s = mfma32(aq[kk % 3], kreg[kk], s);
-            dpv = mfma32(ad[kk % 3], vreg[kk], dpv);
+            s = mfma32(aq[kk % (kLookS + 1)], kreg[kk], s);
+            dpv = mfma32(ad[kk % (kLookS + 1)], vreg[kk], dpv);
         }
     };
 
@@ -237,51 +242,73 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     };
 
     // Element v of P = exp2(S * scale * log2(e) - L2) and dS = P * (dP - D)
-    // into the bf16 A operands of the dV, dK products (k = query). MASK:
-    // zero P where the key is past n_k or (causal) after the query; the
-    // element's query offset 8*(v/4) + v%4 is masked iff it is below lim.
-    auto softmax_elem = [&](auto mask, int v, const f32x16& s, const f32x16& dpv,
-                            const float* lq, const float* dq, int lim, bf16x8* pa, bf16x8* dsa) {
-        float p = fast_exp2(fmaf(s[v], scale2, -lq[v]));
-        if (decltype(mask)::value && 8 * (v >> 2) + (v & 3) < lim) p = 0.0f;
+    // into the bf16 A operands of the dV, dK products (k = query), without
+    // the mask (apply_mask follows on tiles that need it).
+    auto softmax_elem = [&](int v, const f32x16& s, const f32x16& dpv, const float* lq,
+                            const float* dq, bf16x8* pa, bf16x8* dsa) {
+        const float p = fast_exp2(fmaf(s[v], scale2, -lq[v]));
         pa[v >> 3][v & 7] = to_bf16(p);
         dsa[v >> 3][v & 7] = to_bf16(p * (dpv[v] - dq[v]));
+    };
+
+    // Zero P and dS where the key is past n_k or (causal) after the query:
+    // element v (query offset 8*(v/4) + v%4 from q0 + 4g) is masked iff that
+    // offset is below lim. Works on the packed bf16 pairs with bit masks, so
+    // whatever an unmasked element held there (even inf or NaN) is cleared.
+    auto apply_mask = [&](int lim, bf16x8* pa, bf16x8* dsa) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            auto pw = __builtin_bit_cast(uint4, pa[c]);
+            auto dw = __builtin_bit_cast(uint4, dsa[c]);
+            unsigned keep[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int v = 8 * c + 2 * w;   // elements v, v + 1 in word w
+                const int off = 8 * (v >> 2) + (v & 3);
+                keep[w] = (off < lim ? 0u : 0x0000ffffu) | (off + 1 < lim ? 0u : 0xffff0000u);
+            }
+            pw.x &= keep[0]; pw.y &= keep[1]; pw.z &= keep[2]; pw.w &= keep[3];
+            dw.x &= keep[0]; dw.y &= keep[1]; dw.z &= keep[2]; dw.w &= keep[3];
+            pa[c] = __builtin_bit_cast(bf16x8, pw);
+            dsa[c] = __builtin_bit_cast(bf16x8, dw);
+        }
     };
 
     // dV += P^T dO, dK += dS^T Q of one tile (rows = keys, columns = d) from
     // its P, dS operands; the B operands carry queries 16c + 8*(e/4) + 4g +
     // e%4 in slot (g, e), matching the accumulator order of P and dS, and
-    // are read two products ahead. When `mask` is given, the softmax of the
-    // next tile (s, dpv -> pa_n, dsa_n) is computed between the MFMAs, EPM
-    // elements after each.
+    // are read kLookG products ahead. With `with_softmax`, the (unmasked)
+    // softmax of the tile after it (s, dpv -> pa_n, dsa_n) is computed
+    // between the MFMAs, EPM elements after each.
     constexpr int NJ = 2 * NDB;                // (c, db) products of dV and of dK
     constexpr int EPM = 16 / (2 * NJ);         // softmax elements per MFMA
-    auto grads = [&](auto with_softmax, auto mask, const bf16* Qb, const bf16* dOb,
-                     const bf16x8* pa, const bf16x8* dsa, const f32x16& s, const f32x16& dpv,
-                     const float* lq, const float* dq, int lim, bf16x8* pa_n, bf16x8* dsa_n) {
-        bf16x8 bdo[3], bq[3];
-        auto load = [&](int j, int slot) {
-            const int c = j / NDB, db = j % NDB;
-            bdo[slot] = concat(lds_read_tr(&dOb[troff[c][db][0]]), lds_read_tr(&dOb[troff[c][db][1]]));
-            bq[slot] = concat(lds_read_tr(&Qb[troff[c][db][0]]), lds_read_tr(&Qb[troff[c][db][1]]));
+    constexpr int kLookG = 3;
+    auto grads = [&](auto with_softmax, const bf16* Qb, const bf16* dOb, const bf16x8* pa,
+                     const bf16x8* dsa, const f32x16& s, const f32x16& dpv, const float* lq,
+                     const float* dq, bf16x8* pa_n, bf16x8* dsa_n) {
+        bf16x8 bdo[kLookG + 1], bq[kLookG + 1];
+        auto load = [&](int j) {
+            const int c = j / NDB, db = j % NDB, slot = j % (kLookG + 1);
+            bdo[slot] = concat(lds_read_tr(at(dOb, troff[c][db][0])), lds_read_tr(at(dOb, troff[c][db][1])));
+            bq[slot] = concat(lds_read_tr(at(Qb, troff[c][db][0])), lds_read_tr(at(Qb, troff[c][db][1])));
         };
-        load(0, 0);
-        load(1, 1);
+#pragma unroll
+        for (int j = 0; j < kLookG && j < NJ; ++j) load(j);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int c = j / NDB, db = j % NDB;
-            if (j + 2 < NJ) load(j + 2, (j + 2) % 3);
-            dv[db] = mfma32(pa[c], bdo[j % 3], dv[db]);
+            if (j + kLookG < NJ) load(j + kLookG);
+            dv[db] = mfma32(pa[c], bdo[j % (kLookG + 1)], dv[db]);
             if constexpr (decltype(with_softmax)::value) {
 #pragma unroll
                 for (int e = 0; e < EPM; ++e)
-                    softmax_elem(mask, 2 * EPM * j + e, s, dpv, lq, dq, lim, pa_n, dsa_n);
+                    softmax_elem(2 * EPM * j + e, s, dpv, lq, dq, pa_n, dsa_n);
             }
-            dk[db] = mfma32(dsa[c], bq[j % 3], dk[db]);
+            dk[db] = mfma32(dsa[c], bq[j % (kLookG + 1)], dk[db]);
             if constexpr (decltype(with_softmax)::value) {
 #pragma unroll
                 for (int e = 0; e < EPM; ++e)
-                    softmax_elem(mask, 2 * EPM * j + EPM + e, s, dpv, lq, dq, lim, pa_n, dsa_n);
+                    softmax_elem(2 * EPM * j + EPM + e, s, dpv, lq, dq, pa_n, dsa_n);
             }
         }
     };
@@ -296,64 +323,61 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // P and dS of the previous tile (A operands of its dV, dK products).
     bf16x8 pa_p[2], dsa_p[2];
 
-    // One step for tile t: buffers c (tile t), p (tile t-1), f (tile t+1,
+    // One step for tile t: slots c (tile t), p (tile t-1), f (tile t+1,
     // copied during the step). S, dP of tile t on the matrix core; then the
     // dV, dK products of tile t-1 on the matrix core with the softmax of
     // tile t on the VALU between them.
-    auto step = [&](bf16* Qc, bf16* dOc, float* LDc, const bf16* Qp, const bf16* dOp, bf16* Qf,
-                    bf16* dOf, float* LDf, int t) {
-        copies_barrier();  // tile t landed; every wave is done with tile t-2's buffer (f)
-        if (t + 1 < nqt) issue_tile(Qf, dOf, LDf, t + 1);
+    auto step = [&](bf16* Sc, bf16* Sp, bf16* Sf, int t) {
+        copies_barrier();  // tile t landed; every wave is done with tile t-2's slot (f)
+        if (t + 1 < nqt) issue_tile(q_of(Sf), do_of(Sf), ld_of(Sf), t + 1);
         launder_offsets();
         float lq[16], dq[16];
-        read_ld(LDc, lq, dq);
+        read_ld(ld_of(Sc), lq, dq);
         f32x16 s, dpv;
-        scores(Qc, dOc, s, dpv);
-        const int q0 = t * kBQ;
-        const int lim = mask_limit(q0);
+        scores(q_of(Sc), do_of(Sc), s, dpv);
         bf16x8 pa[2], dsa[2];
-        if (needs_mask(q0))
-            grads(yes, yes, Qp, dOp, pa_p, dsa_p, s, dpv, lq, dq, lim, pa, dsa);
-        else
-            grads(yes, no, Qp, dOp, pa_p, dsa_p, s, dpv, lq, dq, lim, pa, dsa);
+        grads(yes, q_of(Sp), do_of(Sp), pa_p, dsa_p, s, dpv, lq, dq, pa, dsa);
+        const int q0 = t * kBQ;
+        if (needs_mask(q0)) apply_mask(mask_limit(q0), pa, dsa);
 #pragma unroll
         for (int c = 0; c < 2; ++c) { pa_p[c] = pa[c]; dsa_p[c] = dsa[c]; }
     };
 
     if (t_begin < nqt) {
-        // Tile t_begin + i is staged in buffer i % 3.
-        issue_tile(Qs0, dOs0, LD0, t_begin);
+        // Tile t_begin + i is staged in slot i % 3.
+        issue_tile(q_of(Sl0), do_of(Sl0), ld_of(Sl0), t_begin);
         copies_barrier();
-        if (t_begin + 1 < nqt) issue_tile(Qs1, dOs1, LD1, t_begin + 1);
+        if (t_begin + 1 < nqt) issue_tile(q_of(Sl1), do_of(Sl1), ld_of(Sl1), t_begin + 1);
         {
             launder_offsets();
             float lq[16], dq[16];
-            read_ld(LD0, lq, dq);
+            read_ld(ld_of(Sl0), lq, dq);
             f32x16 s, dpv;
-            scores(Qs0, dOs0, s, dpv);
-            const int lim = mask_limit(t_begin * kBQ);
+            scores(q_of(Sl0), do_of(Sl0), s, dpv);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) softmax_elem(yes, v, s, dpv, lq, dq, lim, pa_p, dsa_p);
+            for (int v = 0; v < 16; ++v) softmax_elem(v, s, dpv, lq, dq, pa_p, dsa_p);
+            if (needs_mask(t_begin * kBQ)) apply_mask(mask_limit(t_begin * kBQ), pa_p, dsa_p);
         }
-        // Unrolled by three so each step names its buffers at compile time;
+        // Unrolled by three so each step names its slots at compile time;
         // the loop has a single exit, which keeps the dK/dV accumulators in
         // the same registers across the steps.
         for (int t = t_begin + 1; t < nqt; t += 3) {
-            step(Qs1, dOs1, LD1, Qs0, dOs0, Qs2, dOs2, LD2, t);
-            if (t + 1 < nqt) step(Qs2, dOs2, LD2, Qs1, dOs1, Qs0, dOs0, LD0, t + 1);
-            if (t + 2 < nqt) step(Qs0, dOs0, LD0, Qs2, dOs2, Qs1, dOs1, LD1, t + 2);
+            step(Sl1, Sl0, Sl2, t);
+            if (t + 1 < nqt) step(Sl2, Sl1, Sl0, t + 1);
+            if (t + 2 < nqt) step(Sl0, Sl2, Sl1, t + 2);
         }
         // dV, dK of the last tile (already staged; no copy is in flight, so
-        // its buffer may be picked at run time).
+        // its slot may be picked at run time).
         const int slot = (nqt - 1 - t_begin) % 3;
-        const bf16* Ql = slot == 0 ? Qs0 : (slot == 1 ? Qs1 : Qs2);
-        const bf16* dOl = slot == 0 ? dOs0 : (slot == 1 ? dOs1 : dOs2);
+        bf16* Sll = slot == 0 ? Sl0 : (slot == 1 ? Sl1 : Sl2);
+        const bf16* Ql = q_of(Sll);
+        const bf16* dOl = do_of(Sll);
         launder_offsets();
         {
             const f32x16 z = zero_f32x16();
             float lz[16];
             bf16x8 unused[2];
-            grads(no, no, Ql, dOl, pa_p, dsa_p, z, z, lz, lz, 0, unused, unused);
+            grads(no, Ql, dOl, pa_p, dsa_p, z, z, lz, lz, unused, unused);
         }
     }
 

@@ -92,7 +92,11 @@ __device__ __forceinline__ void lds_barrier() {
 // for its own copies (vmcnt) and LDS writes (lgkmcnt), so after the barrier
 // every wave sees every wave's data. Written out because the compiler orders
 // a wave's copy only against that wave's own later reads of the same buffer.
+// The wait is also issued through the builtin (encoding 0x70: vmcnt(0)
+// lgkmcnt(0)), which the compiler's wait insertion sees: it then knows no
+// copy is pending after the barrier and adds no waits of its own for them.
 __device__ __forceinline__ void copies_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x70);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
