@@ -77,321 +77,370 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 }
 
 // --------------------------------------------------------------------------
-// 2. dK, dV: key-stationary, software-pipelined.
+// 2. dK, dV: key-stationary, two waves per group of keys.
 // --------------------------------------------------------------------------
-// One wave per SIMD (the K/V operands and dK/dV accumulators take most of
-// the register file), so the wave overlaps its own work: while the matrix
-// core computes S and dP of query tile t+1, the wave's VALU turns S, dP of
-// tile t into P and dS; then dV, dK of tile t follow. Query tiles stream
-// through a ring of three LDS buffers: t (read by the dV/dK products), t+1
-// (read by the S/dP products) and t+2 (being copied).
+// One workgroup of 8 waves per 128 keys of one (batch, head), as four groups
+// of 32 keys. A group is handled by a pair of waves that share its work:
+//   wave A (waves 0-3) keeps the group's K rows as MFMA operands and the dV
+//     accumulator: S = Q K^T, P = exp2(S * scale * log2(e) - L2),
+//     dV += P^T dO;
+//   wave B (waves 4-7) keeps the group's V rows and the dK accumulator:
+//     dP = dO V^T, dS = P * (dP - D), dK += dS^T Q.
+// Wave A hands P (fp32, in the accumulator layout both waves use) to wave B
+// through LDS. Splitting the group this way halves each wave's registers,
+// so two waves share each SIMD and one issues while the other waits.
+// Query tiles of 32 rows stream through a ring of three LDS slots; a slot
+// also holds the P that wave A computed from its tile, which wave B uses one
+// step later. Within a step each wave overlaps its VALU work (A: the softmax
+// of this tile; B: dS of the previous one) with its MFMAs.
+constexpr int kPairThreads = 512;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
     bf16* __restrict__ dK, bf16* __restrict__ dV,
     int n_q, int n_k, int n_q_pad, int n_ktiles, float scale, float scale2) {
-    constexpr int BKV = 128;           // keys per workgroup (32 per wave)
+    constexpr int BKV = 128;           // keys per workgroup
     constexpr int KK = D / 16;
     constexpr int NDB = D / 32;
+    constexpr int NJ = 2 * NDB;        // (c, db) products of a dV or dK update
     constexpr int TILE = kBQ * D;      // elements per Q or dO tile
-    constexpr int LPW = TILE * 2 / 1024 / 4;  // 1 KB direct copies per wave per tile
+    constexpr int NCH = TILE * 2 / 1024;  // 1 KB copies per tensor and tile
+    constexpr int CPW = 2 * NCH / 8;      // copies per wave and tile
+    static_assert(CPW * 8 == 2 * NCH, "copies split evenly over the waves");
+    constexpr int XW = 64 * 16;        // fp32 words of P per wave pair
 
-    // One LDS object per ring slot, holding the slot's Q tile, dO tile
-    // (row-major, swizzled 16-byte chunks) and the L2, D values of its rows.
+    // One LDS object per ring slot: Q tile, dO tile (row-major, swizzled
+    // 16-byte chunks), L2 and D of the tile's rows, and the four pairs' P.
     // Distinct objects let the compiler tell a slot being copied from slots
-    // being read (it tracks only a few copy targets, so the slot's three
-    // parts share one object).
-    constexpr int SLOT = 2 * TILE + 4 * kBQ;   // bf16 elements per slot
+    // being read (it tracks only a few copy targets).
+    constexpr int SLOT = 2 * TILE + 4 * kBQ + 8 * XW;   // bf16 units
     __shared__ __attribute__((aligned(16))) bf16 Sl0[SLOT];
     __shared__ __attribute__((aligned(16))) bf16 Sl1[SLOT];
     __shared__ __attribute__((aligned(16))) bf16 Sl2[SLOT];
     auto q_of = [](bf16* sl) { return sl; };
     auto do_of = [](bf16* sl) { return sl + TILE; };
     auto ld_of = [](bf16* sl) { return (float*)(sl + 2 * TILE); };
+    auto ex_of = [](bf16* sl) { return (float*)(sl + 2 * TILE + 4 * kBQ); };
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
+    const bool role_a = wave < 4;
+    const int pair = wave & 3;
 
     int bh, kt;   // rank = key tile, ascending: longest causal work first
     work_item(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, &bh, &kt);
     const int k0 = kt * BKV;
-    const int kw0 = k0 + 32 * wave;      // this wave's first key
+    const int kw0 = k0 + 32 * pair;      // the pair's first key
     const int key = kw0 + r;             // this lane's key (column of S, dP)
 
     const bf16* Qh = Q + (size_t)bh * n_q * D;
     const bf16* dOh = dO + (size_t)bh * n_q * D;
-    const bf16* Kh = K + (size_t)bh * n_k * D;
-    const bf16* Vh = V + (size_t)bh * n_k * D;
     const float* l2h = l2p + (size_t)bh * n_q_pad;
     const float* dph = dp + (size_t)bh * n_q_pad;
 
-    // K, V rows of this wave's keys as B operands (column = key, k = d).
-    bf16x8 kreg[KK], vreg[KK];
+    // K (wave A) or V (wave B) rows of the pair's keys as B operands
+    // (column = key, k = d).
+    bf16x8 kv[KK];
     {
+        const bf16* src = (role_a ? K : V) + (size_t)bh * n_k * D;
         const int kc = min(key, n_k - 1);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 kx = *(const bf16x8*)(Kh + kc * D + 16 * kk + 8 * g);
-            const bf16x8 vx = *(const bf16x8*)(Vh + kc * D + 16 * kk + 8 * g);
-            kreg[kk] = key < n_k ? kx : zero_bf16x8();
-            vreg[kk] = key < n_k ? vx : zero_bf16x8();
+            const bf16x8 x = *(const bf16x8*)(src + kc * D + 16 * kk + 8 * g);
+            kv[kk] = key < n_k ? x : zero_bf16x8();
         }
     }
 
-    f32x16 dk[NDB], dv[NDB];
+    // dV (wave A) or dK (wave B) accumulators: rows = keys, columns = d.
+    f32x16 acc[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = zero_f32x16();
+    for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
 
     // Copy query tile t (rows q0 .. q0+31; rows past n_q fall outside the
     // buffer and read as zeros, and their L2 = +inf padding makes P = 0) and
-    // its L2, D values into LDS.
+    // its L2, D values into a slot. Copy b of the tile (Q chunks, then dO
+    // chunks) is issued by wave b % 8.
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, n_q * D * 2);
     const __amdgpu_buffer_rsrc_t dors = make_rsrc(dOh, n_q * D * 2);
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(l2h, n_q_pad * 4);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(dph, n_q_pad * 4);
-    auto issue_tile = [&](bf16* Qd, bf16* dOd, float* LDd, int t) {
+    auto issue_tile = [&](bf16* Sd, int t) {
         const int q0 = t * kBQ;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int b = 4 * i + wave;
-            const int p = 64 * b + lane;
+        for (int i = 0; i < CPW; ++i) {
+            const int b = 8 * i + wave;
+            const bool is_q = b < NCH;
+            const int chunk = is_q ? b : b - NCH;
+            const int p = 64 * chunk + lane;
             const int row = p / (D / 8), pc = p % (D / 8);
-            const int chunk = pc ^ tile_swz<D>(row);
-            const int boff = ((q0 + row) * D + 8 * chunk) * 2;
-            load_lds16(qrs, boff, Qd + 512 * b);
-            load_lds16(dors, boff, dOd + 512 * b);
+            const int boff = ((q0 + row) * D + 8 * (pc ^ tile_swz<D>(row))) * 2;
+            if (is_q) load_lds16(qrs, boff, q_of(Sd) + 512 * chunk);
+            else load_lds16(dors, boff, do_of(Sd) + 512 * chunk);
         }
-        // lanes 0-7: 8 x 16 B of L2 into LDd[0..31]; lanes 8-15: D into
-        // LDd[32..63] (q0 is a multiple of 32 < n_q_pad)
+        // lanes 0-7: 8 x 16 B of L2 into LD[0..31]; lanes 8-15: D into
+        // LD[32..63] (q0 is a multiple of 32 < n_q_pad)
         if (wave == 0) {
-            if (lane < 8) load_lds16(lrs, (q0 + 4 * lane) * 4, LDd);
-            else if (lane < 16) load_lds16(drs, (q0 + 4 * (lane - 8)) * 4, LDd);
+            if (lane < 8) load_lds16(lrs, (q0 + 4 * lane) * 4, ld_of(Sd));
+            else if (lane < 16) load_lds16(drs, (q0 + 4 * (lane - 8)) * 4, ld_of(Sd));
         }
     };
 
     // Per-lane byte offsets of the LDS operand reads, the same for every
-    // buffer. Each step passes them through an empty asm so that the
-    // buffer's base is added inside the step and folds into the read's
-    // immediate offset (otherwise every buffer/offset pair is hoisted out of
-    // the loop into a register of its own).
-    //  soff[kk]:       Q / dO row r, k-step kk (A operands of S and dP);
-    //  troff[c][j][h]: transpose reads for dV / dK, B operand of product
-    //                  (c, db = j), rows 16c + 4g + s16/4 + 8h.
+    // slot. Each step passes them through an empty asm so that the slot's
+    // base is added inside the step and folds into the read's immediate
+    // offset (otherwise every slot/offset pair is hoisted out of the loop
+    // into a register of its own).
+    //  soff[kk]:     tile row r, k-step kk (A operands of S and dP);
+    //  troff[db][h]: transpose reads (B operands of dV and dK) of product
+    //                (c, db), rows 16c + 4g + s16/4 + 8h; c = 1 adds 16
+    //                rows, which keeps the swizzle, so it is a constant.
     int soff[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) soff[kk] = 2 * tile_off<D>(r, 16 * kk + 8 * g);
-    int troff[2][NDB][2];
+    int troff[NDB][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                troff[c][db][h] = 2 * tile_off<D>(16 * c + 4 * g + (s16 >> 2) + 8 * h,
-                                                  32 * db + 16 * half + 4 * (s16 & 3));
-    auto at = [](const bf16* base, int byte_off) {
-        return (const bf16*)((const char*)base + byte_off);
-    };
+        for (int h = 0; h < 2; ++h)
+            troff[db][h] = 2 * tile_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * half + 4 * (s16 & 3));
+    static_assert(tile_swz<D>(16) == tile_swz<D>(0) && tile_swz<D>(17) == tile_swz<D>(1) &&
+                      tile_swz<D>(18) == tile_swz<D>(2) && tile_swz<D>(19) == tile_swz<D>(3),
+                  "16 rows down keeps the swizzle");
     auto launder_offsets = [&]() {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(troff[c][db][h]));
+            for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(troff[db][h]));
+    };
+    auto at = [](const bf16* base, int byte_off) {
+        return (const bf16*)((const char*)base + byte_off);
     };
 
-    // S = Q K^T and dP = dO V^T of one staged tile (rows = queries, columns
-    // = keys). Lane holds key kw0 + r; element v is query q0 + acc_row(v, g).
-    // The Q, dO operands are read kLookS k-steps ahead of their MFMAs.
+    // Scheduling: the operand loops below are each a region of their own
+    // (sched_barrier), with the order of reads, MFMAs and the VALU work
+    // handed in pinned by group barriers: left to itself the scheduler
+    // moves every LDS read next to the MFMA that uses it, which exposes the
+    // read's latency on every MFMA.
+    constexpr int kDsRead = 0x100, kMfma = 0x008, kValu = 0x402;  // VALU incl. transcendental
+
+    // acc_s = T kv^T for a staged Q or dO tile T: rows = queries, columns =
+    // the pair's keys; lane holds key kw0 + r, element v is query
+    // q0 + acc_row(v, g). Tile operands are read kLookS k-steps ahead;
+    // extra(kk) runs after the MFMA of k-step kk and issues about NV VALU
+    // instructions.
     constexpr int kLookS = 3;
-    auto scores = [&](const bf16* Qb, const bf16* dOb, f32x16& s, f32x16& dpv) {
-        s = zero_f32x16();
-        dpv = zero_f32x16();
-        bf16x8 aq[kLookS + 1], ad[kLookS + 1];
+    auto rows_times_keys = [&](const bf16* Tb, f32x16& acc_s, auto&& extra, auto nv) {
+        constexpr int NV = decltype(nv)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        acc_s = zero_f32x16();
+        bf16x8 a[kLookS + 1];
 #pragma unroll
-        for (int kk = 0; kk < kLookS && kk < KK; ++kk) {
-            aq[kk] = *(const bf16x8*)at(Qb, soff[kk]);
-            ad[kk] = *(const bf16x8*)at(dOb, soff[kk]);
-        }
+        for (int kk = 0; kk < kLookS && kk < KK; ++kk) a[kk] = *(const bf16x8*)at(Tb, soff[kk]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            if (kk + kLookS < KK) {
-                aq[(kk + kLookS) % (kLookS + 1)] = *(const bf16x8*)at(Qb, soff[kk + kLookS]);
-                ad[(kk + kLookS) % (kLookS + 1)] = *(const bf16x8*)at(dOb, soff[kk + kLookS]);
-            }
-            s = mfma32(aq[kk % (kLookS + 1)], kreg[kk], s);
-            dpv = mfma32(ad[kk % (kLookS + 1)], vreg[kk], dpv);
+            if (kk + kLookS < KK)
+                a[(kk + kLookS) % (kLookS + 1)] = *(const bf16x8*)at(Tb, soff[kk + kLookS]);
+            acc_s = mfma32(a[kk % (kLookS + 1)], kv[kk], acc_s);
+            extra(kk);
         }
-    };
-
-    // L2 and D of the 16 queries this lane's accumulator elements hold:
-    // element v = 4i + j is query q0 + 8i + 4g + j.
-    auto read_ld = [&](const float* LDb, float* lq, float* dq) {
+        __builtin_amdgcn_sched_group_barrier(kDsRead, kLookS, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 l4 = *(const float4*)(&LDb[8 * i + 4 * g]);
-            const float4 d4 = *(const float4*)(&LDb[kBQ + 8 * i + 4 * g]);
-            lq[4 * i] = l4.x; lq[4 * i + 1] = l4.y; lq[4 * i + 2] = l4.z; lq[4 * i + 3] = l4.w;
-            dq[4 * i] = d4.x; dq[4 * i + 1] = d4.y; dq[4 * i + 2] = d4.z; dq[4 * i + 3] = d4.w;
+        for (int kk = 0; kk < KK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            if (NV > 0) __builtin_amdgcn_sched_group_barrier(kValu, NV, 0);
+            if (kk + kLookS < KK) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Element v of P = exp2(S * scale * log2(e) - L2) and dS = P * (dP - D)
-    // into the bf16 A operands of the dV, dK products (k = query), without
-    // the mask (apply_mask follows on tiles that need it).
-    auto softmax_elem = [&](int v, const f32x16& s, const f32x16& dpv, const float* lq,
-                            const float* dq, bf16x8* pa, bf16x8* dsa) {
-        const float p = fast_exp2(fmaf(s[v], scale2, -lq[v]));
-        pa[v >> 3][v & 7] = to_bf16(p);
-        dsa[v >> 3][v & 7] = to_bf16(p * (dpv[v] - dq[v]));
-    };
-
-    // Zero P and dS where the key is past n_k or (causal) after the query:
-    // element v (query offset 8*(v/4) + v%4 from q0 + 4g) is masked iff that
-    // offset is below lim. Works on the packed bf16 pairs with bit masks, so
-    // whatever an unmasked element held there (even inf or NaN) is cleared.
-    auto apply_mask = [&](int lim, bf16x8* pa, bf16x8* dsa) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            auto pw = __builtin_bit_cast(uint4, pa[c]);
-            auto dw = __builtin_bit_cast(uint4, dsa[c]);
-            unsigned keep[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int v = 8 * c + 2 * w;   // elements v, v + 1 in word w
-                const int off = 8 * (v >> 2) + (v & 3);
-                keep[w] = (off < lim ? 0u : 0x0000ffffu) | (off + 1 < lim ? 0u : 0xffff0000u);
-            }
-            pw.x &= keep[0]; pw.y &= keep[1]; pw.z &= keep[2]; pw.w &= keep[3];
-            dw.x &= keep[0]; dw.y &= keep[1]; dw.z &= keep[2]; dw.w &= keep[3];
-            pa[c] = __builtin_bit_cast(bf16x8, pw);
-            dsa[c] = __builtin_bit_cast(bf16x8, dw);
-        }
-    };
-
-    // dV += P^T dO, dK += dS^T Q of one tile (rows = keys, columns = d) from
-    // its P, dS operands; the B operands carry queries 16c + 8*(e/4) + 4g +
-    // e%4 in slot (g, e), matching the accumulator order of P and dS, and
-    // are read kLookG products ahead. With `with_softmax`, the (unmasked)
-    // softmax of the tile after it (s, dpv -> pa_n, dsa_n) is computed
-    // between the MFMAs, EPM elements after each.
-    constexpr int NJ = 2 * NDB;                // (c, db) products of dV and of dK
-    constexpr int EPM = 16 / (2 * NJ);         // softmax elements per MFMA
+    // acc[db] += X^T T for a staged Q or dO tile T (rows = keys, columns =
+    // d), X = P or dS as A operands (k = query). The B operands carry queries
+    // 16c + 8*(e/4) + 4g + e%4 in slot (g, e), matching the accumulator order
+    // of P and dS, and are read kLookG products ahead; extra(j) runs after
+    // product j and issues about NV VALU instructions.
     constexpr int kLookG = 3;
-    auto grads = [&](auto with_softmax, const bf16* Qb, const bf16* dOb, const bf16x8* pa,
-                     const bf16x8* dsa, const f32x16& s, const f32x16& dpv, const float* lq,
-                     const float* dq, bf16x8* pa_n, bf16x8* dsa_n) {
-        bf16x8 bdo[kLookG + 1], bq[kLookG + 1];
+    auto keys_times_tile = [&](const bf16* Tb, const bf16x8* xa, auto&& extra, auto nv) {
+        constexpr int NV = decltype(nv)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 b[kLookG + 1];
         auto load = [&](int j) {
-            const int c = j / NDB, db = j % NDB, slot = j % (kLookG + 1);
-            bdo[slot] = concat(lds_read_tr(at(dOb, troff[c][db][0])), lds_read_tr(at(dOb, troff[c][db][1])));
-            bq[slot] = concat(lds_read_tr(at(Qb, troff[c][db][0])), lds_read_tr(at(Qb, troff[c][db][1])));
+            const int cb = (j / NDB) * 16 * D * 2, db = j % NDB;
+            b[j % (kLookG + 1)] = concat(lds_read_tr(at(Tb, troff[db][0] + cb)),
+                                         lds_read_tr(at(Tb, troff[db][1] + cb)));
         };
 #pragma unroll
         for (int j = 0; j < kLookG && j < NJ; ++j) load(j);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int c = j / NDB, db = j % NDB;
             if (j + kLookG < NJ) load(j + kLookG);
-            dv[db] = mfma32(pa[c], bdo[j % (kLookG + 1)], dv[db]);
-            if constexpr (decltype(with_softmax)::value) {
+            acc[j % NDB] = mfma32(xa[j / NDB], b[j % (kLookG + 1)], acc[j % NDB]);
+            extra(j);
+        }
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * kLookG, 0);
 #pragma unroll
-                for (int e = 0; e < EPM; ++e)
-                    softmax_elem(2 * EPM * j + e, s, dpv, lq, dq, pa_n, dsa_n);
-            }
-            dk[db] = mfma32(dsa[c], bq[j % (kLookG + 1)], dk[db]);
-            if constexpr (decltype(with_softmax)::value) {
+        for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            if (NV > 0) __builtin_amdgcn_sched_group_barrier(kValu, NV, 0);
+            if (j + kLookG < NJ) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // 16 fp32 values of this lane's queries (element v = 4i + j is query
+    // q0 + 8i + 4g + j) from a slot's L2 (part 0) or D (part 1) array.
+    auto read_rows = [&](const float* LDb, int part, float* x) {
 #pragma unroll
-                for (int e = 0; e < EPM; ++e)
-                    softmax_elem(2 * EPM * j + EPM + e, s, dpv, lq, dq, pa_n, dsa_n);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const float4 f = *(const float4*)(&LDb[kBQ * part + 8 * i + 4 * g]);
+            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+        }
+    };
+    // P exchange: word i (4 floats) of lane l of pair p at p*XW + 256i + 4l,
+    // so each 16-byte access of a wave covers 1 KB contiguously.
+    auto write_p = [&](bf16* Sd, const float* p) {
+        float* ex = ex_of(Sd) + pair * XW + 4 * lane;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(float4*)(ex + 256 * i) = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+    };
+    auto read_p = [&](bf16* Sd, float* p) {
+        const float* ex = ex_of(Sd) + pair * XW + 4 * lane;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 f = *(const float4*)(ex + 256 * i);
+            p[4 * i] = f.x; p[4 * i + 1] = f.y; p[4 * i + 2] = f.z; p[4 * i + 3] = f.w;
         }
     };
 
     const int nqt = (n_q + kBQ - 1) / kBQ;
     const int t_begin = CAUSAL ? k0 / kBQ : 0;
-    const std::true_type yes{};
-    const std::false_type no{};
-    auto mask_limit = [&](int q0) { return key >= n_k ? 64 : (CAUSAL ? key - q0 - 4 * g : -1); };
-    auto needs_mask = [&](int q0) { return (kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0); };
+    auto noop = [](int) {};
+    const std::integral_constant<int, 0> nv0{};
+    // VALU instructions per MFMA of wave A's softmax (fma, exp per element).
+    const std::integral_constant<int, 2 * (16 / NJ)> nv_softmax{};
 
-    // P and dS of the previous tile (A operands of its dV, dK products).
-    bf16x8 pa_p[2], dsa_p[2];
-
-    // One step for tile t: slots c (tile t), p (tile t-1), f (tile t+1,
-    // copied during the step). S, dP of tile t on the matrix core; then the
-    // dV, dK products of tile t-1 on the matrix core with the softmax of
-    // tile t on the VALU between them.
-    auto step = [&](bf16* Sc, bf16* Sp, bf16* Sf, int t) {
-        copies_barrier();  // tile t landed; every wave is done with tile t-2's slot (f)
-        if (t + 1 < nqt) issue_tile(q_of(Sf), do_of(Sf), ld_of(Sf), t + 1);
-        launder_offsets();
-        float lq[16], dq[16];
-        read_ld(ld_of(Sc), lq, dq);
-        f32x16 s, dpv;
-        scores(q_of(Sc), do_of(Sc), s, dpv);
-        bf16x8 pa[2], dsa[2];
-        grads(yes, q_of(Sp), do_of(Sp), pa_p, dsa_p, s, dpv, lq, dq, pa, dsa);
-        const int q0 = t * kBQ;
-        if (needs_mask(q0)) apply_mask(mask_limit(q0), pa, dsa);
+    // Wave A's P of tile t (q0 = t * kBQ): zero where the key is past n_k or
+    // (causal) after the query (element v's query offset 8*(v/4) + v%4 from
+    // q0 + 4g is masked iff below lim), hand the fp32 values to wave B
+    // through slot Sd and keep them as bf16 A operands for dV.
+    auto finish_p = [&](int q0, float* p, bf16* Sd, bf16x8* pa) {
+        if ((kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0)) {
+            const int lim = key >= n_k ? 64 : (CAUSAL ? key - q0 - 4 * g : -1);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) { pa_p[c] = pa[c]; dsa_p[c] = dsa[c]; }
+            for (int v = 0; v < 16; ++v)
+                if (8 * (v >> 2) + (v & 3) < lim) p[v] = 0.0f;
+        }
+        write_p(Sd, p);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pa[v >> 3][v & 7] = to_bf16(p[v]);
     };
 
     if (t_begin < nqt) {
         // Tile t_begin + i is staged in slot i % 3.
-        issue_tile(q_of(Sl0), do_of(Sl0), ld_of(Sl0), t_begin);
+        issue_tile(Sl0, t_begin);
         copies_barrier();
-        if (t_begin + 1 < nqt) issue_tile(q_of(Sl1), do_of(Sl1), ld_of(Sl1), t_begin + 1);
-        {
-            launder_offsets();
-            float lq[16], dq[16];
-            read_ld(ld_of(Sl0), lq, dq);
-            f32x16 s, dpv;
-            scores(q_of(Sl0), do_of(Sl0), s, dpv);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) softmax_elem(v, s, dpv, lq, dq, pa_p, dsa_p);
-            if (needs_mask(t_begin * kBQ)) apply_mask(mask_limit(t_begin * kBQ), pa_p, dsa_p);
-        }
-        // Unrolled by three so each step names its slots at compile time;
-        // the loop has a single exit, which keeps the dK/dV accumulators in
-        // the same registers across the steps.
-        for (int t = t_begin + 1; t < nqt; t += 3) {
-            step(Sl1, Sl0, Sl2, t);
-            if (t + 1 < nqt) step(Sl2, Sl1, Sl0, t + 1);
-            if (t + 2 < nqt) step(Sl0, Sl2, Sl1, t + 2);
-        }
-        // dV, dK of the last tile (already staged; no copy is in flight, so
-        // its slot may be picked at run time).
-        const int slot = (nqt - 1 - t_begin) % 3;
-        bf16* Sll = slot == 0 ? Sl0 : (slot == 1 ? Sl1 : Sl2);
-        const bf16* Ql = q_of(Sll);
-        const bf16* dOl = do_of(Sll);
+        if (t_begin + 1 < nqt) issue_tile(Sl1, t_begin + 1);
         launder_offsets();
-        {
-            const f32x16 z = zero_f32x16();
-            float lz[16];
-            bf16x8 unused[2];
-            grads(no, Ql, dOl, pa_p, dsa_p, z, z, lz, lz, unused, unused);
+        const int t_last = nqt - 1;
+        const int s_last = (t_last - t_begin) % 3;
+        if (role_a) {
+            // P of the previous tile (A operands of its dV update).
+            bf16x8 pa_p[2];
+            {
+                float lq[16], p[16];
+                read_rows(ld_of(Sl0), 0, lq);
+                f32x16 s;
+                rows_times_keys(q_of(Sl0), s, noop, nv0);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(s[v], scale2, -lq[v]));
+                finish_p(t_begin * kBQ, p, Sl0, pa_p);
+            }
+            // Step for tile t: slots c (tile t), p (t-1), f (t+1, copied
+            // during the step). S of tile t, then dV of tile t-1 with the
+            // softmax of tile t between its MFMAs.
+            auto step = [&](bf16* Sc, bf16* Sp, bf16* Sf, int t) {
+                copies_barrier();  // tile t landed; everyone is done with slot f (tile t-2)
+                if (t + 1 < nqt) issue_tile(Sf, t + 1);
+                launder_offsets();
+                float lq[16], p[16];
+                read_rows(ld_of(Sc), 0, lq);
+                f32x16 s;
+                rows_times_keys(q_of(Sc), s, noop, nv0);
+                constexpr int EPM = 16 / NJ;
+                keys_times_tile(do_of(Sp), pa_p, [&](int j) {
+#pragma unroll
+                    for (int e = 0; e < EPM; ++e) {
+                        const int v = EPM * j + e;
+                        p[v] = fast_exp2(fmaf(s[v], scale2, -lq[v]));
+                    }
+                }, nv_softmax);
+                finish_p(t * kBQ, p, Sc, pa_p);
+            };
+            // Unrolled by three so each step names its slots at compile
+            // time; a single loop exit keeps the accumulators in place.
+            for (int t = t_begin + 1; t < nqt; t += 3) {
+                step(Sl1, Sl0, Sl2, t);
+                if (t + 1 < nqt) step(Sl2, Sl1, Sl0, t + 1);
+                if (t + 2 < nqt) step(Sl0, Sl2, Sl1, t + 2);
+            }
+            copies_barrier();  // pairs with wave B's wait for the last P
+            bf16* Sl = s_last == 0 ? Sl0 : (s_last == 1 ? Sl1 : Sl2);
+            launder_offsets();
+            keys_times_tile(do_of(Sl), pa_p, noop, nv0);
+        } else {
+            // dP of the previous tile (its dS is formed one step later).
+            f32x16 dp_c;
+            rows_times_keys(do_of(Sl0), dp_c, noop, nv0);
+            // Step for tile t: dS of tile t-1 (from wave A's P, dP and D of
+            // t-1), dP of tile t, then dK of tile t-1. The dS work runs while
+            // wave A of the same SIMD keeps the matrix core busy.
+            auto step = [&](bf16* Sc, bf16* Sp, bf16* Sf, int t) {
+                copies_barrier();  // tile t landed; P of tile t-1 written
+                if (t + 1 < nqt) issue_tile(Sf, t + 1);
+                launder_offsets();
+                float dq[16], p[16];
+                read_rows(ld_of(Sp), 1, dq);
+                read_p(Sp, p);
+                bf16x8 dsa[2];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * (dp_c[v] - dq[v]));
+                rows_times_keys(do_of(Sc), dp_c, noop, nv0);
+                keys_times_tile(q_of(Sp), dsa, noop, nv0);
+            };
+            for (int t = t_begin + 1; t < nqt; t += 3) {
+                step(Sl1, Sl0, Sl2, t);
+                if (t + 1 < nqt) step(Sl2, Sl1, Sl0, t + 1);
+                if (t + 2 < nqt) step(Sl0, Sl2, Sl1, t + 2);
+            }
+            copies_barrier();  // P of the last tile written
+            bf16* Sl = s_last == 0 ? Sl0 : (s_last == 1 ? Sl1 : Sl2);
+            launder_offsets();
+            float dq[16], p[16];
+            read_rows(ld_of(Sl), 1, dq);
+            read_p(Sl, p);
+            bf16x8 dsa[2];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * (dp_c[v] - dq[v]));
+            keys_times_tile(q_of(Sl), dsa, noop, nv0);
         }
     }
 
-    // Epilogue: dK = scale * acc; rows = keys kw0 + acc_row(v, g), column = d.
+    // Epilogue: wave A stores dV, wave B stores dK = scale * acc; rows =
+    // keys kw0 + acc_row(v, g), column = d.
+    bf16* out = role_a ? dV : dK;
+    const float f = role_a ? 1.0f : scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int kr = kw0 + acc_row(v, g);
-            if (kr < n_k) {
-                const size_t off = ((size_t)bh * n_k + kr) * D + 32 * db + r;
-                dK[off] = to_bf16(dk[db][v] * scale);
-                dV[off] = to_bf16(dv[db][v]);
-            }
+            if (kr < n_k) out[((size_t)bh * n_k + kr) * D + 32 * db + r] = to_bf16(acc[db][v] * f);
         }
 }
 
@@ -572,7 +621,7 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 1, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * n_ktiles)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * n_ktiles)), dim3(kPairThreads), 0,
                        st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o,
                        (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dk, (bf16*)a.dv,
                        a.n_q, a.n_k, n_q_pad, n_ktiles, a.scale, a.scale * kLog2e);

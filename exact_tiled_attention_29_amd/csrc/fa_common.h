@@ -126,7 +126,7 @@ __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
 // bank groups, and (b) 4 consecutive rows (aligned to 4) read over 4
 // consecutive chunks (a transpose read) hit disjoint banks.
 template <int D>
-__device__ __forceinline__ int tile_swz(int rho) {
+__host__ __device__ constexpr int tile_swz(int rho) {
     static_assert(D == 64 || D == 128, "head dim");
     if constexpr (D == 128) return (4 * (rho & 3)) ^ ((rho >> 2) & 3);
     else return (4 * ((rho >> 1) & 1)) ^ ((rho >> 2) & 3);
