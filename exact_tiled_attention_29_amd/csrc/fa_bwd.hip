@@ -210,7 +210,13 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     static_assert(tile_swz<D>(16) == tile_swz<D>(0) && tile_swz<D>(17) == tile_swz<D>(1) &&
                       tile_swz<D>(18) == tile_swz<D>(2) && tile_swz<D>(19) == tile_swz<D>(3),
                   "16 rows down keeps the swizzle");
+    //  ldoff:        L2 / D values of the lane's queries, 4g floats in;
+    //  exoff:        the lane's P words in the exchange area.
+    int ldoff = 2 * 2 * TILE + 4 * 4 * g;
+    int exoff = 2 * (2 * TILE + 4 * kBQ) + 4 * (pair * XW + 4 * lane);
     auto launder_offsets = [&]() {
+        asm volatile("" : "+v"(ldoff));
+        asm volatile("" : "+v"(exoff));
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
 #pragma unroll
@@ -293,24 +299,25 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     };
 
     // 16 fp32 values of this lane's queries (element v = 4i + j is query
-    // q0 + 8i + 4g + j) from a slot's L2 (part 0) or D (part 1) array.
-    auto read_rows = [&](const float* LDb, int part, float* x) {
+    // q0 + 8i + 4g + j) from slot Sd's L2 (part 0) or D (part 1) array.
+    auto read_rows = [&](bf16* Sd, int part, float* x) {
+        const float* ld = (const float*)at(Sd, ldoff);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float4 f = *(const float4*)(&LDb[kBQ * part + 8 * i + 4 * g]);
+            const float4 f = *(const float4*)(ld + kBQ * part + 8 * i);
             x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
         }
     };
     // P exchange: word i (4 floats) of lane l of pair p at p*XW + 256i + 4l,
     // so each 16-byte access of a wave covers 1 KB contiguously.
     auto write_p = [&](bf16* Sd, const float* p) {
-        float* ex = ex_of(Sd) + pair * XW + 4 * lane;
+        float* ex = (float*)at(Sd, exoff);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             *(float4*)(ex + 256 * i) = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
     };
     auto read_p = [&](bf16* Sd, float* p) {
-        const float* ex = ex_of(Sd) + pair * XW + 4 * lane;
+        const float* ex = (const float*)at(Sd, exoff);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float4 f = *(const float4*)(ex + 256 * i);
@@ -318,12 +325,68 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
         }
     };
 
+    // One step's MFMAs of a wave as a single operand stream: KK products
+    // acc1 = T1 kv^T (operands read from tile T1 by rows), then NJ products
+    // acc[db] += X^T T2 (operands read from tile T2 by transpose). Operands
+    // are read kLook stream positions ahead, across the change of tile, so
+    // the second phase starts with its operands in registers. pre() issues
+    // NPRE other LDS reads first; extra1(kk) / extra2(j) run after the MFMAs
+    // of the two phases with about NV1 / NV2 VALU instructions each.
+    constexpr int kLook = 4;
+    auto stream = [&](const bf16* T1, f32x16& acc1, const bf16* T2, const bf16x8* X, auto&& pre,
+                      auto npre, auto&& extra1, auto nv1, auto&& extra2, auto nv2) {
+        constexpr int NPRE = decltype(npre)::value;
+        constexpr int NV1 = decltype(nv1)::value, NV2 = decltype(nv2)::value;
+        constexpr int NS = KK + NJ;
+        __builtin_amdgcn_sched_barrier(0);
+        pre();
+        bf16x8 op[kLook + 1];
+        auto load = [&](int i) {
+            if (i < KK) {
+                op[i % (kLook + 1)] = *(const bf16x8*)at(T1, soff[i]);
+            } else {
+                const int j = i - KK, cb = (j / NDB) * 16 * D * 2, db = j % NDB;
+                op[i % (kLook + 1)] = concat(lds_read_tr(at(T2, troff[db][0] + cb)),
+                                             lds_read_tr(at(T2, troff[db][1] + cb)));
+            }
+        };
+        acc1 = zero_f32x16();
+#pragma unroll
+        for (int i = 0; i < kLook; ++i) load(i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (i + kLook < NS) load(i + kLook);
+            if (i < KK) {
+                acc1 = mfma32(op[i % (kLook + 1)], kv[i], acc1);
+                extra1(i);
+            } else {
+                const int j = i - KK;
+                acc[j % NDB] = mfma32(X[j / NDB], op[i % (kLook + 1)], acc[j % NDB]);
+                extra2(j);
+            }
+        }
+        // DS read instructions per stream position: 1 (row read), 2 (transpose)
+        constexpr int FIRST = NPRE + (kLook <= KK ? kLook : KK + 2 * (kLook - KK));
+        __builtin_amdgcn_sched_group_barrier(kDsRead, FIRST, 0);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            if (i < KK && NV1 > 0) __builtin_amdgcn_sched_group_barrier(kValu, NV1, 0);
+            if (i >= KK && NV2 > 0) __builtin_amdgcn_sched_group_barrier(kValu, NV2, 0);
+            if (i + kLook < KK) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+            else if (i + kLook < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     const int nqt = (n_q + kBQ - 1) / kBQ;
     const int t_begin = CAUSAL ? k0 / kBQ : 0;
     auto noop = [](int) {};
     const std::integral_constant<int, 0> nv0{};
+    auto none = []() {};
     // VALU instructions per MFMA of wave A's softmax (fma, exp per element).
     const std::integral_constant<int, 2 * (16 / NJ)> nv_softmax{};
+    const std::integral_constant<int, 4> n_row_reads{};
 
     // Wave A's P of tile t (q0 = t * kBQ): zero where the key is past n_k or
     // (causal) after the query (element v's query offset 8*(v/4) + v%4 from
@@ -354,7 +417,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
             bf16x8 pa_p[2];
             {
                 float lq[16], p[16];
-                read_rows(ld_of(Sl0), 0, lq);
+                read_rows(Sl0, 0, lq);
                 f32x16 s;
                 rows_times_keys(q_of(Sl0), s, noop, nv0);
 #pragma unroll
@@ -369,11 +432,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
                 if (t + 1 < nqt) issue_tile(Sf, t + 1);
                 launder_offsets();
                 float lq[16], p[16];
-                read_rows(ld_of(Sc), 0, lq);
                 f32x16 s;
-                rows_times_keys(q_of(Sc), s, noop, nv0);
                 constexpr int EPM = 16 / NJ;
-                keys_times_tile(do_of(Sp), pa_p, [&](int j) {
+                stream(q_of(Sc), s, do_of(Sp), pa_p, [&]() { read_rows(Sc, 0, lq); }, n_row_reads,
+                       noop, nv0, [&](int j) {
 #pragma unroll
                     for (int e = 0; e < EPM; ++e) {
                         const int v = EPM * j + e;
@@ -405,13 +467,12 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
                 if (t + 1 < nqt) issue_tile(Sf, t + 1);
                 launder_offsets();
                 float dq[16], p[16];
-                read_rows(ld_of(Sp), 1, dq);
+                read_rows(Sp, 1, dq);
                 read_p(Sp, p);
                 bf16x8 dsa[2];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * (dp_c[v] - dq[v]));
-                rows_times_keys(do_of(Sc), dp_c, noop, nv0);
-                keys_times_tile(q_of(Sp), dsa, noop, nv0);
+                stream(do_of(Sc), dp_c, q_of(Sp), dsa, none, nv0, noop, nv0, noop, nv0);
             };
             for (int t = t_begin + 1; t < nqt; t += 3) {
                 step(Sl1, Sl0, Sl2, t);
@@ -422,7 +483,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
             bf16* Sl = s_last == 0 ? Sl0 : (s_last == 1 ? Sl1 : Sl2);
             launder_offsets();
             float dq[16], p[16];
-            read_rows(ld_of(Sl), 1, dq);
+            read_rows(Sl, 1, dq);
             read_p(Sl, p);
             bf16x8 dsa[2];
 #pragma unroll
@@ -521,25 +582,74 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
     const int wave_last_row = min(qw + RW, n_q) - 1;
 
+    // Per-lane byte offsets of the LDS operand reads, the same for both
+    // buffers and both 32-key halves (32 and 16 rows down keep the
+    // swizzle, so those are constants); passed through an empty asm in each
+    // tile step so the buffer's base folds into the reads' immediate offsets.
+    //  soff[kk]:     K / V row r, k-step kk (A operands of S^T and dP^T);
+    //  troff[db][h]: transpose reads of K (A operands of dQ^T), rows
+    //                4g + s16/4 + 8h (+ 16c + 32kb), columns of block db.
+    int soff[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) soff[kk] = 2 * tile_off<D>(r, 16 * kk + 8 * g);
+    int troff[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            troff[db][h] = 2 * tile_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * half + 4 * (s16 & 3));
+    static_assert(tile_swz<D>(16) == tile_swz<D>(0) && tile_swz<D>(17) == tile_swz<D>(1) &&
+                      tile_swz<D>(18) == tile_swz<D>(2) && tile_swz<D>(19) == tile_swz<D>(3),
+                  "16 rows down keeps the swizzle");
+    auto at = [](const bf16* base, int byte_off) {
+        return (const bf16*)((const char*)base + byte_off);
+    };
+
+    // Zero dS^T where the key is past n_k or (causal) after the query:
+    // element v (key offset 8*(v/4) + v%4 from ks + 32kb + 4g) is masked iff
+    // that offset is >= lim. Works on the packed bf16 pairs with bit masks.
+    auto apply_mask = [&](int lim, bf16x8* ds) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            auto w = __builtin_bit_cast(uint4, ds[c]);
+            unsigned keep[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int v = 8 * c + 2 * i;   // elements v, v + 1 in word i
+                const int off = 8 * (v >> 2) + (v & 3);
+                keep[i] = (off >= lim ? 0u : 0x0000ffffu) | (off + 1 >= lim ? 0u : 0xffff0000u);
+            }
+            w.x &= keep[0]; w.y &= keep[1]; w.z &= keep[2]; w.w &= keep[3];
+            ds[c] = __builtin_bit_cast(bf16x8, w);
+        }
+    };
+
     auto tile_step = [&](const bf16* Kb, const bf16* Vb, int ks) {
         const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row);
         if (!active) return;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(troff[db][h]));
         const bool need_mask = (ks + kBC > n_k) || (CAUSAL && ks + kBC - 1 > qw);
         // Two 32-key halves, one after the other, to keep fewer values live.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            const int rb = kb * 32 * D * 2;   // byte offset of the half's rows
             mfma_priority(true);
             // S^T = K Q^T and dP^T = V dO^T (rows = keys, columns = queries);
             // K and V operands are read one k-step ahead of their MFMAs.
             f32x16 s = zero_f32x16(), dpt = zero_f32x16();
             bf16x8 ak[2], av[2];
-            ak[0] = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 8 * g)]);
-            av[0] = *(const bf16x8*)(&Vb[tile_off<D>(32 * kb + r, 8 * g)]);
+            ak[0] = *(const bf16x8*)at(Kb, soff[0] + rb);
+            av[0] = *(const bf16x8*)at(Vb, soff[0] + rb);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 if (kk + 1 < KK) {
-                    ak[(kk + 1) & 1] = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 16 * (kk + 1) + 8 * g)]);
-                    av[(kk + 1) & 1] = *(const bf16x8*)(&Vb[tile_off<D>(32 * kb + r, 16 * (kk + 1) + 8 * g)]);
+                    ak[(kk + 1) & 1] = *(const bf16x8*)at(Kb, soff[kk + 1] + rb);
+                    av[(kk + 1) & 1] = *(const bf16x8*)at(Vb, soff[kk + 1] + rb);
                 }
                 s = mfma32(ak[kk & 1], qreg[kk], s);
                 dpt = mfma32(av[kk & 1], doreg[kk], dpt);
@@ -547,24 +657,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             sched_reads_ahead_of_mfma<KK>();
             mfma_priority(false);
             // key of element v: ks + 32kb + 4g + 8*(v/4) + v%4 (see the forward)
-            const int lim = (CAUSAL ? min(n_k, row + 1) : n_k) - ks - 32 * kb - 4 * g;
             bf16x8 dsb[2];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                float p = fast_exp2(fmaf(s[v], scale2, -l2));
-                if (need_mask && 8 * (v >> 2) + (v & 3) >= lim) p = 0.0f;
+                const float p = fast_exp2(fmaf(s[v], scale2, -l2));
                 dsb[v >> 3][v & 7] = to_bf16(p * (dpt[v] - drw));
             }
+            if (need_mask)
+                apply_mask((CAUSAL ? min(n_k, row + 1) : n_k) - ks - 32 * kb - 4 * g, dsb);
             // dQ^T (d x queries) += K^T dS^T; K^T operands by transpose reads.
             mfma_priority(true);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const int col = 32 * db + 16 * half + 4 * (s16 & 3);
-                    const int row0 = 32 * kb + 16 * c + 4 * g + (s16 >> 2);
-                    const bf16x8 a = concat(lds_read_tr(&Kb[tile_off<D>(row0, col)]),
-                                            lds_read_tr(&Kb[tile_off<D>(row0 + 8, col)]));
+                    const int cb = rb + c * 16 * D * 2;
+                    const bf16x8 a = concat(lds_read_tr(at(Kb, troff[db][0] + cb)),
+                                            lds_read_tr(at(Kb, troff[db][1] + cb)));
                     acc[db] = mfma32(a, dsb[c], acc[db]);
                 }
             mfma_priority(false);
