@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     constexpr int XW = 64 * 16;        // fp32 words of P per wave pair
 
     // One LDS object per ring slot: Q tile, dO tile (row-major, swizzled
-    // 16-byte chunks), L2 and D of the tile's rows, and the four pairs' P.
+    // 16-byte chunks), L2 and D of the tile's rows, and the four pairs' P
+    // (at byte 2 * (2 * TILE + 4 * kBQ); see exoff below).
     // Distinct objects let the compiler tell a slot being copied from slots
     // being read (it tracks only a few copy targets).
     constexpr int SLOT = 2 * TILE + 4 * kBQ + 8 * XW;   // bf16 units
@@ -122,7 +123,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     auto q_of = [](bf16* sl) { return sl; };
     auto do_of = [](bf16* sl) { return sl + TILE; };
     auto ld_of = [](bf16* sl) { return (float*)(sl + 2 * TILE); };
-    auto ex_of = [](bf16* sl) { return (float*)(sl + 2 * TILE + 4 * kBQ); };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

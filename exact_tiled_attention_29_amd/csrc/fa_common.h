@@ -158,22 +158,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Scheduling hint for the pipelined step "S^T of the next tile under the
-// softmax of this one": KK k-steps of 2 LDS reads + 2 MFMAs, with the
-// softmax's VALU work spread between the MFMAs.
-template <int KK>
-__device__ __forceinline__ void sched_scores_under_softmax() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);      // K reads of k-steps 0, 1
-#pragma unroll
-    for (int i = 0; i < KK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);  // VALU
-        if (i + 2 < KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // reads of step i + 2
-    }
-}
-
 // 16-byte global -> LDS copy that bypasses registers (buffer_load_dwordx4 ...
 // lds): lane l's 16 bytes, read at byte offset `voff` of the resource, land at
 // lds_base + 16*l; lds_base must be wave-uniform. A buffer (not a flat/global)

@@ -110,31 +110,72 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     const int wave_last_row = min(qw + RW, n_q) - 1;  // < qw when the wave has no rows
 
+    // Per-lane byte offsets of the LDS operand reads, the same for both
+    // buffers; 32 and 16 rows down keep the swizzle, so the second 32-key
+    // block and the 16-key groups of the PV product are immediates. Passed
+    // through an empty asm in each tile step so the buffer's base folds into
+    // the reads' immediate offsets (otherwise every buffer/offset pair is
+    // hoisted out of the loop into a register of its own).
+    //  soff[kk]:     K row r, k-step kk (A operands of S^T);
+    //  troff[db][h]: transpose reads of V (A operands of O^T), rows
+    //                4g + s16/4 + 8h (+ 16c), columns of block db.
+    int soff[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) soff[kk] = 2 * tile_off<D>(r, 16 * kk + 8 * g);
+    int troff[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            troff[db][h] = 2 * tile_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * half + 4 * (s16 & 3));
+    static_assert(tile_swz<D>(16) == tile_swz<D>(0) && tile_swz<D>(17) == tile_swz<D>(1) &&
+                      tile_swz<D>(18) == tile_swz<D>(2) && tile_swz<D>(19) == tile_swz<D>(3),
+                  "16 rows down keeps the swizzle");
+    auto at = [](const bf16* base, int byte_off) {
+        return (const bf16*)((const char*)base + byte_off);
+    };
+
     // Compute on one staged tile (K rows in Kb, V rows in Vb).
     auto tile_step = [&](const bf16* Kb, const bf16* Vb, int ks) {
         const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row);
         if (active) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(troff[db][h]));
             // S^T (keys x queries) for two 32-key blocks. K operands are read
-            // one k-step ahead, so each step's LDS reads overlap the previous
-            // step's MFMAs.
+            // kLook k-steps ahead of their MFMAs (order pinned below: the
+            // scheduler would otherwise move each read next to its MFMA).
+            constexpr int kLook = 2;
             f32x16 s[2];
             s[0] = s[1] = zero_f32x16();
-            bf16x8 ka[2][2];
+            bf16x8 ka[kLook + 1][2];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                ka[0][kb] = *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 8 * g)]);
+            for (int kk = 0; kk < kLook; ++kk)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    ka[kk][kb] = *(const bf16x8*)at(Kb, soff[kk] + kb * 32 * D * 2);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                if (kk + 1 < KK) {
+                if (kk + kLook < KK) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
-                        ka[(kk + 1) & 1][kb] =
-                            *(const bf16x8*)(&Kb[tile_off<D>(32 * kb + r, 16 * (kk + 1) + 8 * g)]);
+                        ka[(kk + kLook) % (kLook + 1)][kb] =
+                            *(const bf16x8*)at(Kb, soff[kk + kLook] + kb * 32 * D * 2);
                 }
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[kk & 1][kb], qreg[kk], s[kb]);
+                for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[kk % (kLook + 1)][kb], qreg[kk], s[kb]);
             }
-            sched_reads_ahead_of_mfma<KK>();
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 0);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (kk + kLook < KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // Mask keys past n_k and (causal) keys after the query: the key of
             // element v is ks + 32*kb + 4g + 8*(v/4) + v%4, so one compare of a
             // constant against a per-lane limit decides it.
@@ -183,10 +224,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             for (int c = 0; c < 4; ++c) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const int col = 32 * db + 16 * half + 4 * (s16 & 3);
-                    const int row0 = 16 * c + 4 * g + (s16 >> 2);
-                    const bf16x8 a = concat(lds_read_tr(&Vb[tile_off<D>(row0, col)]),
-                                            lds_read_tr(&Vb[tile_off<D>(row0 + 8, col)]));
+                    const int cb = c * 16 * D * 2;
+                    const bf16x8 a = concat(lds_read_tr(at(Vb, troff[db][0] + cb)),
+                                            lds_read_tr(at(Vb, troff[db][1] + cb)));
                     o[db] = mfma32(a, pb[c], o[db]);
                 }
             }
