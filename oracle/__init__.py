@@ -5,5 +5,6 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_head,
     online_softmax_stats,
+    row_softmax,
     softmax_three_pass,
 )

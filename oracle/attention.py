@@ -29,8 +29,10 @@ head the full score rows are materialised, in chunks of query rows taken at
 full key width (a softmax row never spans two chunks; dK and dV are sums over
 rows, so chunking them is exact).
 
-Also here, for pinning only: the one-pass running (m, l) statistics of page 1,
-section 1 (online_softmax_stats) and page 3, section 1.1.
+Also here: the one-pass running (m, l) statistics of page 1, section 1
+(online_softmax_stats) and page 3, section 1.1, and the row softmax /
+logsumexp of a plain matrix (row_softmax) that the standalone row kernel
+computes.
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ import numpy as np
 __all__ = [
     "online_softmax_stats",
     "softmax_three_pass",
+    "row_softmax",
     "attention_head",
     "attention_forward",
     "attention_backward",
@@ -77,6 +80,28 @@ def softmax_three_pass(S):
     E = np.exp(S - m[:, None])
     l = E.sum(axis=1)
     return E / l[:, None], m, l
+
+
+def row_softmax(X, scale=1.0):
+    """Softmax and natural-log logsumexp of each row of scale * X (page 1,
+    section 1: the softmax of a score row and its logsumexp, compared there
+    against torch.softmax / torch.logsumexp), by the three-pass definition.
+
+    A row whose entries are all -inf has no defined softmax; here it gets
+    P = 0 and L = -inf (the pages leave it open; the row kernel does the
+    same). Returns (P, L) as float64 arrays.
+    """
+    S = np.asarray(X, dtype=np.float64) * float(scale)
+    if S.ndim != 2 or S.shape[1] == 0:
+        raise ValueError("X must be 2-D with at least one column")
+    P = np.zeros_like(S)
+    L = np.full(S.shape[0], -math.inf)
+    live = np.isfinite(S.max(axis=1)) if S.shape[0] else np.zeros(0, bool)
+    if live.any():
+        Pl, m, l = softmax_three_pass(S[live])
+        P[live] = Pl
+        L[live] = m + np.log(l)
+    return P, L
 
 
 def _scores(Qr, K, row_ids, causal, scale):

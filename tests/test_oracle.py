@@ -379,3 +379,67 @@ def test_planted_output_mistakes_are_caught(kind):
                 r["dV"] = E.T @ dO
         return r
     assert not _pins_pass(fn)
+
+
+# --------------------------------------------------------- row softmax / logsumexp
+# oracle.row_softmax is the definition the standalone row kernel follows
+# (page 1, section 1). Pins: SciPy's logsumexp / softmax, closed forms,
+# masked entries, overflow-prone magnitudes and the one-pass statistics.
+
+def _row_pins(fn):
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((37, 301)) * 3.0
+    for scale in (1.0, 0.125, 2.5):
+        P, L = fn(X, scale)
+        assert np.allclose(L, scipy.special.logsumexp(X * scale, axis=1), rtol=0, atol=1e-12)
+        assert np.allclose(P, scipy.special.softmax(X * scale, axis=1), rtol=0, atol=1e-14)
+    # constant rows: P = 1/n, L = ln n + scale * c
+    n = 64
+    C = np.tile(np.arange(5, dtype=np.float64)[:, None], (1, n))
+    P, L = fn(C, 0.5)
+    assert np.allclose(P, 1.0 / n, atol=1e-15)
+    assert np.allclose(L, math.log(n) + 0.5 * np.arange(5), atol=1e-12)
+    # -inf entries drop out; an all -inf row gives P = 0, L = -inf
+    Y = rng.standard_normal((3, 10))
+    Y[0, ::2] = -np.inf
+    Y[2, :] = -np.inf
+    P, L = fn(Y, 1.0)
+    assert np.allclose(P[0, 1::2], scipy.special.softmax(Y[0, 1::2]), atol=1e-14)
+    assert (P[0, ::2] == 0).all()
+    assert (P[2] == 0).all() and L[2] == -math.inf
+    assert np.isclose(L[1], scipy.special.logsumexp(Y[1]), atol=1e-12)
+    # magnitudes that overflow exp without the max shift
+    Z = np.array([[1000.0, 999.0, 998.0], [-1000.0, -1001.0, -1002.0]])
+    P, L = fn(Z, 1.0)
+    ref = np.log(1 + math.exp(-1) + math.exp(-2))
+    assert np.allclose(L, [1000 + ref, -1000 + ref], atol=1e-9)
+    assert np.allclose(P[0], P[1], atol=1e-15)
+
+
+def test_row_softmax_pins():
+    _row_pins(oracle.row_softmax)
+
+
+@pytest.mark.parametrize("block", [1, 7, 64, 301])
+def test_row_softmax_matches_one_pass_stats(block):
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((5, 301)) * 4.0
+    _, L = oracle.row_softmax(X, 0.25)
+    for i in range(5):
+        m, l = oracle.online_softmax_stats(X[i] * 0.25, block)
+        assert abs(L[i] - (m + math.log(l))) < 1e-12
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "log2", "no_shift_sum", "unnormalised"])
+def test_planted_row_softmax_mistakes_are_caught(kind):
+    def mutant(X, scale=1.0):
+        P, L = oracle.row_softmax(X, 1.0 if kind == "no_scale" else scale)
+        if kind == "log2":
+            L = L / math.log(2)
+        if kind == "no_shift_sum":
+            L = L + 1.0
+        if kind == "unnormalised":
+            P = P * 1.01
+        return P, L
+    with pytest.raises(AssertionError):
+        _row_pins(mutant)
