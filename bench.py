@@ -13,6 +13,7 @@ the timed region) and the fp64 CPU oracle timed on a bounded sample of the
 same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --rows [--rows-shape RxC]   # standalone row softmax kernel (HBM roofline)
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --summary-out F   # HBM bytes per kernel
   python bench.py --summarize-stats DIR --summary-out F                  # kernel durations
 """
@@ -149,6 +150,59 @@ def cpu_baseline(w, q, k, v, do, n_heads):
 
 
 # --------------------------------------------------------------------------
+# Standalone row softmax / logsumexp kernel
+# --------------------------------------------------------------------------
+
+def bench_rows(args):
+    """Times fa_row_softmax (softmax + logsumexp of every row) on a bf16
+    matrix resident in HBM; the roofline is HBM: one read of x, one write of
+    y and of L per call."""
+    import numpy as np
+    import torch
+    import exact_tiled_attention_29_amd as fa
+
+    rows, cols = (int(t) for t in args.rows_shape.lower().split("x"))
+    dev = torch.device("cuda:0")
+    fa.load_library()
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = (torch.randn(rows, cols, generator=g, device=dev) * 3.0).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    scale = 1.0 / np.sqrt(128.0)
+    run = lambda: fa.row_softmax(x, scale, True, torch.bfloat16, lse=lse, out=y)  # noqa: E731
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / K
+    nbytes = rows * cols * 2 * 2 + rows * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] row softmax {rows}x{cols} bf16: {ms:.4f} ms/call -> {gbs:.0f} GB/s "
+        f"({100 * gbs / 8000:.1f}% of 8000)")
+    result = {
+        "metric": "row softmax + logsumexp GB/s (bf16)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,9) bf16 rows)",
+        "config": {"workload": f"rows_{rows}x{cols}_bf16", "rows": rows, "cols": cols},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": None, "kernel": "row_softmax",
+                     "avg_ms": round(ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+# --------------------------------------------------------------------------
 # GPU benchmark
 # --------------------------------------------------------------------------
 
@@ -167,6 +221,11 @@ def main():
     ap.add_argument("--summary-out", default=PMC_SUMMARY)
     ap.add_argument("--summary-copy-mib", type=int, default=512)
     ap.add_argument("--summary-command", default="", help="command line recorded in a summary")
+    ap.add_argument("--rows", action="store_true",
+                    help="benchmark the standalone row softmax / logsumexp kernel instead")
+    ap.add_argument("--rows-shape", default="262144x4096",
+                    help="rows x cols of the row kernel's bf16 input (default: the score rows of "
+                         "the 2x32x4096 workload)")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -187,6 +246,9 @@ def main():
     import torch
     import exact_tiled_attention_29_amd as fa
     import workloads
+
+    if args.rows:
+        return bench_rows(args)
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]

@@ -7,9 +7,10 @@ the current HIP stream. There is no CPU fallback: without the built library
 or without a GPU the calls raise.
 
 The C functions are re-exported under their own names (fa_fwd, fa_bwd,
-fa_bwd_workspace_bytes, fa_status_str, fa_abi_version), taking plain ints
-for pointers. The tensor-level helpers are forward(), backward() and the
-autograd wrapper FlashAttention / attention().
+fa_bwd_timed, fa_bwd_workspace_bytes, fa_row_softmax, fa_status_str,
+fa_abi_version), taking plain ints for pointers. The tensor-level helpers
+are forward(), backward(), row_softmax() and the autograd wrapper
+FlashAttention / attention().
 """
 from __future__ import annotations
 
@@ -21,8 +22,9 @@ import torch  # imported before libfa.so so the process shares torch's HIP runti
 
 __all__ = [
     "FA_BF16", "FA_F32", "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version",
-    "forward", "backward", "FlashAttention", "attention",
+    "fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_row_softmax",
+    "fa_status_str", "fa_abi_version",
+    "forward", "backward", "row_softmax", "FlashAttention", "attention",
 ]
 
 FA_BF16 = 0
@@ -64,6 +66,8 @@ def load_library():
     lib.fa_bwd.restype = i32
     lib.fa_bwd_timed.argtypes = lib.fa_bwd.argtypes + [vp]
     lib.fa_bwd_timed.restype = i32
+    lib.fa_row_softmax.argtypes = [vp, i32, ctypes.c_longlong, i32, f32, vp, vp, i32, vp]
+    lib.fa_row_softmax.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -93,6 +97,10 @@ def fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n
     return load_library().fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads,
                                        n_q, n_k, d, dtype, int(causal), float(scale), workspace,
                                        workspace_bytes, stream, events)
+
+
+def fa_row_softmax(x, dtype, rows, cols, scale, lse, y, y_dtype, stream):
+    return load_library().fa_row_softmax(x, dtype, rows, cols, float(scale), lse, y, y_dtype, stream)
 
 
 def fa_bwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, causal):
@@ -207,6 +215,35 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
     if st != 0:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def row_softmax(x, scale=1.0, softmax=True, y_dtype=None, lse=None, out=None):
+    """Row logsumexp (and softmax) of scale * x over its last dimension.
+
+    x: contiguous bf16 or fp32 GPU tensor of shape [..., cols]. Returns
+    (y, lse): y the softmax rows in y_dtype (default x.dtype), or None when
+    softmax=False; lse fp32 of shape x.shape[:-1] (natural log)."""
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise TypeError("x must be a tensor with at least one dimension")
+    dt = _code(x.dtype)
+    _check(x, "x", tuple(x.shape))
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if lse is None:
+        lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lse, "lse", tuple(x.shape[:-1]), torch.float32)
+    y = None
+    ydt = FA_BF16
+    if softmax:
+        y_dtype = x.dtype if y_dtype is None else y_dtype
+        ydt = _code(y_dtype)
+        y = torch.empty(x.shape, dtype=y_dtype, device=x.device) if out is None else out
+        _check(y, "out", tuple(x.shape), y_dtype)
+    st = fa_row_softmax(x.data_ptr(), dt, rows, cols, scale, lse.data_ptr(),
+                        y.data_ptr() if y is not None else None, ydt, _stream(x.device))
+    if st != 0:
+        raise FAError(st, "fa_row_softmax")
+    return y, lse
 
 
 class FlashAttention(torch.autograd.Function):

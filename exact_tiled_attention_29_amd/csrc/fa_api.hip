@@ -138,5 +138,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, int o_dty
                         dtype, causal, scale, workspace, workspace_bytes_given, stream, nullptr);
 }
 
+int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float scale, float* lse,
+                   void* y, int y_dtype, void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_DTYPE;
+    if (y_dtype != FA_BF16 && y_dtype != FA_F32) return FA_E_DTYPE;
+    if (rows < 0 || cols < 0) return FA_E_SHAPE;
+    if (!(isfinite(scale) && scale > 0.0f)) return FA_E_SCALE;
+    if (rows == 0) return FA_OK;
+    if (cols == 0 || rows > (1LL << 40) / cols) return FA_E_SHAPE;
+    if (!x || !lse) return FA_E_NULLPTR;
+    fa::RowArgs a;
+    a.x = x; a.rows = rows; a.cols = cols; a.x_f32 = dtype == FA_F32; a.scale = scale;
+    a.lse = lse; a.y = y; a.y_f32 = y_dtype == FA_F32;
+    return hip_status(fa::launch_row_softmax(a, (hipStream_t)stream));
+}
+
 }  // extern "C"
 

@@ -58,6 +58,19 @@ int fwd_bf16_rows_per_wg(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st);
 
+// Row softmax / logsumexp of a [rows, cols] matrix (see fa_rows.hip).
+struct RowArgs {
+    const void* x;
+    long long rows;
+    int cols;
+    bool x_f32;   // x float32 (else bf16)
+    float scale;
+    float* lse;   // [rows] fp32
+    void* y;      // NULL or [rows, cols]
+    bool y_f32;   // y float32 (else bf16)
+};
+hipError_t launch_row_softmax(const RowArgs& a, hipStream_t st);
+
 // Zero `bytes` bytes (a multiple of 4) with a fill kernel; no memset node,
 // so the call is safe under stream capture.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);

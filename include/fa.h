@@ -125,6 +125,29 @@ int fa_bwd_timed(const void* q, const void* k, const void* v,
                  void* workspace, size_t workspace_bytes, void* stream,
                  void* const* events);
 
+/*
+ * Row softmax and logsumexp of a plain matrix: for every row r of scale * X,
+ * lse[r] = ln sum_c exp(scale * X[r,c]) and, when y is not NULL,
+ * y[r,c] = exp(scale * X[r,c] - lse[r]).
+ *
+ * Defined by: the softmax of a score row and its logsumexp, computed in one
+ * pass with a running max m and a sum l rebased to it (page 1,
+ * "05_flash_attention.py", section 1, online softmax; page 3, "Flash
+ * Attention", section 1.1); lse = m + ln l.
+ *
+ * x      [rows, cols] dtype (FA_BF16 or FA_F32), read once for lse and once
+ *        more for y.
+ * lse    [rows] float32 (required).
+ * y      NULL (lse only) or [rows, cols] y_dtype (FA_BF16, rounded to
+ *        nearest even, or FA_F32).
+ * rows   >= 0 (0 is an empty call); cols >= 1 when rows > 0.
+ * scale  finite, > 0.
+ * A row whose entries are all -inf gets lse = -inf and a zero y row. NaN or
+ * +inf entries give undefined results for their row.
+ */
+int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float scale,
+                   float* lse, void* y, int y_dtype, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 

@@ -37,8 +37,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_status_str",
-         "fa_abi_version"])
+        ["fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_row_softmax",
+         "fa_status_str", "fa_abi_version"])
 
 
 def test_library_exports_every_header_function(lib):
@@ -123,6 +123,28 @@ def test_workspace_bytes(lib):
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, 0, d, BF16, 0) == 0
 
 
+def rows_call(**kw):
+    args = dict(x=P, dtype=BF16, rows=4, cols=8, scale=1.0, lse=P, y=P, y_dtype=BF16, stream=None)
+    args.update(kw)
+    return fa.fa_row_softmax(**args)
+
+
+def test_row_softmax_validation_codes(lib):
+    assert rows_call(dtype=2) == DTYPE
+    assert rows_call(y_dtype=-1) == DTYPE
+    assert rows_call(rows=-1) == SHAPE
+    assert rows_call(cols=-2) == SHAPE
+    assert rows_call(cols=0) == SHAPE
+    assert rows_call(rows=1 << 40, cols=2) == SHAPE
+    assert rows_call(scale=0.0) == SCALE
+    assert rows_call(scale=float("nan")) == SCALE
+    assert rows_call(x=None) == NULLPTR
+    assert rows_call(lse=None) == NULLPTR
+    # nothing to compute: returns before any HIP call
+    assert rows_call(rows=0, x=None, lse=None, y=None) == OK
+    assert rows_call(rows=0, cols=0) == OK
+
+
 def test_python_helpers_refuse_cpu_tensors(lib):
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
@@ -130,3 +152,5 @@ def test_python_helpers_refuse_cpu_tensors(lib):
         fa.forward(q, q, q)
     with pytest.raises(TypeError):
         fa.forward(q.half(), q.half(), q.half())
+    with pytest.raises(ValueError, match="GPU"):
+        fa.row_softmax(q)

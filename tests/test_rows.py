@@ -1,0 +1,122 @@
+"""GPU parity of the standalone row softmax / logsumexp kernel (C ABI
+fa_row_softmax) against the fp64 oracle (oracle.row_softmax).
+
+Tolerances follow from the arithmetic: each lane sums ceil(cols / 64)
+exponentials sequentially in fp32 before a 6-level butterfly, so the relative
+error of the row sum l is at most about (cols / 64 + 6) * 2^-24 plus the
+exp2 instruction's error (~2^-22 per term, relative); |dL| <= 2e-4 covers
+cols up to 1e5 with margin. Softmax values are compared relative to their
+size: 3e-4 for fp32 output, plus the bf16 unit roundoff (2^-8: 8
+significant bits, round to nearest even) for bf16 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import exact_tiled_attention_29_amd as fa
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+    yield
+    torch.cuda.empty_cache()
+
+
+TOL_L = 2e-4
+
+
+def _inputs(rows, cols, dtype, seed, sigma=3.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(rows, cols, generator=g) * sigma
+    return x.to(dtype)
+
+
+def _check(x, scale, y_dtype, tag):
+    xg = x.cuda()
+    y, lse = fa.row_softmax(xg, scale, True, y_dtype)
+    torch.cuda.synchronize()
+    P, L = oracle.row_softmax(x.double().numpy(), scale)
+    Lg = lse.cpu().double().numpy()
+    fin = np.isfinite(L)
+    assert (np.isneginf(Lg) == ~fin).all(), tag
+    assert np.abs(Lg[fin] - L[fin]).max(initial=0) <= TOL_L, (tag, np.abs(Lg[fin] - L[fin]).max())
+    yg = y.cpu().double().numpy()
+    rel = 3e-4 + (2.0 ** -8 if y_dtype == torch.bfloat16 else 0.0)
+    err = np.abs(yg - P) - rel * P
+    assert err.max(initial=0) <= 1e-7, (tag, err.max())
+
+
+SHAPES = [(1, 1), (3, 7), (5, 8), (4, 63), (17, 1000), (64, 4096), (6, 4104), (8, 32768),
+          (2, 100003), (9, 4), (9, 5), (130, 512)]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_row_softmax_shapes(rows, cols, dtype):
+    x = _inputs(rows, cols, dtype, seed=rows * 31 + cols)
+    _check(x, 1.0, dtype, (rows, cols, dtype))
+
+
+@pytest.mark.parametrize("y_dtype", [torch.bfloat16, torch.float32])
+def test_row_softmax_scale_and_output_dtype(y_dtype):
+    x = _inputs(33, 777, torch.bfloat16, seed=5)
+    _check(x, 0.0883883, y_dtype, ("scale", y_dtype))
+    x = _inputs(33, 768, torch.float32, seed=6)
+    _check(x, 2.5, y_dtype, ("scale", y_dtype))
+
+
+@pytest.mark.parametrize("cols", [40, 512])
+def test_row_softmax_neg_inf_rows_and_entries(cols):
+    x = _inputs(6, cols, torch.bfloat16, seed=7)
+    x[0, ::3] = -float("inf")
+    x[2, :] = -float("inf")
+    x[4, 1:] = -float("inf")      # one finite entry: softmax is one-hot
+    _check(x, 1.0, torch.float32, ("-inf", cols))
+    y, lse = fa.row_softmax(x.cuda(), 1.0, True, torch.float32)
+    y = y.cpu()
+    assert (y[2] == 0).all() and lse[2].item() == -float("inf")
+    assert y[4, 0].item() == 1.0 and (y[4, 1:] == 0).all()
+
+
+def test_row_softmax_large_magnitudes():
+    x = torch.tensor([[1000.0, 999.0, 998.0, -5.0] * 16, [-1000.0, -1001.0, -1002.0, -2000.0] * 16])
+    _check(x, 1.0, torch.float32, "magnitudes")
+
+
+def test_row_softmax_lse_only_and_batched_shape():
+    x = _inputs(2 * 3 * 50, 96, torch.bfloat16, seed=8).reshape(2, 3, 50, 96)
+    y, lse = fa.row_softmax(x.cuda(), 0.5, softmax=False)
+    assert y is None and lse.shape == (2, 3, 50)
+    _, L = oracle.row_softmax(x.reshape(-1, 96).double().numpy(), 0.5)
+    assert np.abs(lse.cpu().reshape(-1).double().numpy() - L).max() <= TOL_L
+
+
+def test_row_softmax_empty():
+    x = torch.zeros(0, 16, dtype=torch.bfloat16, device="cuda")
+    y, lse = fa.row_softmax(x)
+    assert y.shape == (0, 16) and lse.shape == (0,)
+
+
+def test_row_softmax_bench_size_sampled():
+    # The bench workload (262144 x 4096 bf16, attention-score rows of the
+    # 2x32x4096 workload): sampled rows against the oracle, and every row's
+    # softmax sums to 1 within the output rounding.
+    rows, cols = 262144, 4096
+    g = torch.Generator(device="cuda").manual_seed(9)
+    x = (torch.randn(rows, cols, generator=g, device="cuda") * 3.0).to(torch.bfloat16)
+    y, lse = fa.row_softmax(x, 0.0883883, True, torch.bfloat16)
+    s = y.float().sum(dim=1)
+    assert (s - 1).abs().max().item() <= 2.0 ** -8 + 1e-3   # sum of rounding errors <= u * sum(y)
+    idx = torch.tensor([0, 1, 4095, 4096, 131071, 262143] + list(range(7, rows, 9973)))
+    P, L = oracle.row_softmax(x[idx].cpu().double().numpy(), 0.0883883)
+    assert np.abs(lse[idx].cpu().double().numpy() - L).max() <= TOL_L
+    err = np.abs(y[idx].cpu().double().numpy() - P) - (3e-4 + 2.0 ** -8) * P
+    assert err.max() <= 1e-7
