@@ -556,6 +556,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
     const float l2 = row < n_q ? l2p[(size_t)bh * n_q_pad + row] : __builtin_huge_valf();
     const float drw = row < n_q ? dp[(size_t)bh * n_q_pad + row] : 0.0f;
+    // Every element of a lane's dP^T accumulator belongs to the lane's query,
+    // so the accumulator starts at -D and the MFMAs deliver dP - D directly.
+    f32x16 neg_d;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) neg_d[v] = -drw;
 
     int kend = n_k;
     if (CAUSAL) kend = min(n_k, min(q0 + BR, n_q));
@@ -639,9 +644,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         for (int kb = 0; kb < 2; ++kb) {
             const int rb = kb * 32 * D * 2;   // byte offset of the half's rows
             mfma_priority(true);
-            // S^T = K Q^T and dP^T = V dO^T (rows = keys, columns = queries);
-            // K and V operands are read one k-step ahead of their MFMAs.
-            f32x16 s = zero_f32x16(), dpt = zero_f32x16();
+            // S^T = K Q^T and dP^T - D = V dO^T - D (rows = keys, columns =
+            // queries); K and V operands are read one k-step ahead.
+            f32x16 s = zero_f32x16(), dpt = neg_d;
             bf16x8 ak[2], av[2];
             ak[0] = *(const bf16x8*)at(Kb, soff[0] + rb);
             av[0] = *(const bf16x8*)at(Vb, soff[0] + rb);
@@ -661,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float p = fast_exp2(fmaf(s[v], scale2, -l2));
-                dsb[v >> 3][v & 7] = to_bf16(p * (dpt[v] - drw));
+                dsb[v >> 3][v & 7] = to_bf16(p * dpt[v]);
             }
             if (need_mask)
                 apply_mask((CAUSAL ? min(n_k, row + 1) : n_k) - ks - 32 * kb - 4 * g, dsb);
