@@ -4,6 +4,7 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward,
     attention_head,
+    causal_offset,
     online_softmax_stats,
     row_softmax,
     softmax_three_pass,

@@ -12,6 +12,13 @@ What is computed, and where the pages define it:
 * The causal mask is top-left aligned: key j is visible to query i iff j <= i,
   also when n_q != n_k (page 1, "05_flash_attention.py", section 2,
   standard_attention masks triu(1) of the n x m score matrix).
+* The bottom-right aligned causal mask is a variant the pages do not define:
+  key j is visible to query i iff j <= i + (n_k - n_q), i.e. the last query
+  sees every key, as when the queries are the newest n_q positions of an
+  n_k-long sequence. For n_q == n_k it is the top-left mask. When n_q > n_k
+  the first n_q - n_k queries see no key; a softmax over no entries is
+  undefined, and here such a row gets O = 0, L = -inf and adds nothing to
+  any gradient (its dQ is 0), the same convention as row_softmax.
 * Softmax is the three-pass safe softmax: row max, exponentials of the
   shifted scores and their sum, then normalisation (page 2, section
   块内归一化; page 3, "Flash Attention", section 1.1).
@@ -44,6 +51,7 @@ __all__ = [
     "online_softmax_stats",
     "softmax_three_pass",
     "row_softmax",
+    "causal_offset",
     "attention_head",
     "attention_forward",
     "attention_backward",
@@ -104,13 +112,27 @@ def row_softmax(X, scale=1.0):
     return P, L
 
 
-def _scores(Qr, K, row_ids, causal, scale):
+def causal_offset(causal, n_q, n_k):
+    """Diagonal offset of the causal mask: key j is visible to query i iff
+    j <= i + offset. None for no mask; 0 for the top-left mask (causal True,
+    1 or "top_left"); n_k - n_q for the bottom-right mask (2 or
+    "bottom_right")."""
+    if causal is False or causal is None or (not isinstance(causal, str) and causal == 0):
+        return None
+    if causal is True or causal == "top_left" or (not isinstance(causal, str) and causal == 1):
+        return 0
+    if causal == "bottom_right" or (not isinstance(causal, str) and causal == 2):
+        return n_k - n_q
+    raise ValueError(f"unknown causal mode {causal!r}")
+
+
+def _scores(Qr, K, row_ids, off, scale):
     """S = scale * Qr K^T for the query rows row_ids (global indices), with
-    the top-left causal mask applied as -inf."""
+    keys j > i + off masked as -inf (off None: no mask)."""
     S = scale * (Qr @ K.T)
-    if causal:
+    if off is not None:
         key_ids = np.arange(K.shape[0])
-        S[key_ids[None, :] > row_ids[:, None]] = -np.inf
+        S[key_ids[None, :] > row_ids[:, None] + off] = -np.inf
     return S
 
 
@@ -119,6 +141,8 @@ def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=N
     """Exact attention for one head, in float64.
 
     Q: (n_q, d); K, V: (n_k, d); dO: (n_q, d) or None for forward only.
+    causal: False (no mask), True / "top_left", or "bottom_right" (see
+    causal_offset).
     rows: query indices whose O, L (and dQ) are returned (default: all).
     cols: key indices whose dK, dV are returned (default: all).
 
@@ -153,15 +177,17 @@ def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=N
     else:
         visit = np.unique(rows)
 
+    off = causal_offset(causal, n_q, n_k)
     for c0 in range(0, len(visit), row_chunk):
         ids = visit[c0:c0 + row_chunk]
-        S = _scores(Q[ids], K, ids, causal, scale)
-        P, m, l = softmax_three_pass(S)
+        S = _scores(Q[ids], K, ids, off, scale)
+        # rows that see no key (bottom-right mask, n_q > n_k): P = 0, L = -inf
+        P, Lc = row_softmax(S)
         keep = np.array([int(r) in out_pos for r in ids])
         if keep.any():
             pos = np.array([out_pos[int(r)] for r in ids[keep]])
             O[pos] = P[keep] @ V
-            L[pos] = m[keep] + np.log(l[keep])
+            L[pos] = Lc[keep]
         if want_bwd:
             dOc = dO[ids]
             dP = dOc @ V.T

@@ -296,6 +296,150 @@ def test_block_diagonal_sketch_differs_from_exact():
 
 
 # --------------------------------------------------------------------------
+# bottom-right aligned causal mask (a variant the pages leave open: key j is
+# visible to query i iff j <= i + n_k - n_q; rows that see no key give
+# O = 0, L = -inf, dQ = 0 and add nothing to dK, dV)
+# --------------------------------------------------------------------------
+
+def _visible_counts(n_q, n_k, off):
+    return np.clip(np.arange(n_q) + off + 1, 0, n_k)
+
+
+BR_SHAPES = [(37, 37), (50, 130), (130, 50), (1, 9), (9, 1), (12, 9)]
+
+
+@pytest.mark.parametrize("n_q,n_k", BR_SHAPES)
+def test_causal_offsets(n_q, n_k):
+    assert oracle.causal_offset(False, n_q, n_k) is None
+    assert oracle.causal_offset(0, n_q, n_k) is None
+    assert oracle.causal_offset(True, n_q, n_k) == 0
+    assert oracle.causal_offset("top_left", n_q, n_k) == 0
+    assert oracle.causal_offset("bottom_right", n_q, n_k) == n_k - n_q
+    assert oracle.causal_offset(2, n_q, n_k) == n_k - n_q
+    with pytest.raises(ValueError):
+        oracle.causal_offset("diagonal", n_q, n_k)
+
+
+@pytest.mark.parametrize("n_q,n_k", BR_SHAPES)
+@pytest.mark.parametrize("chunk", [5, 256])
+def test_bottom_right_zero_query_gives_suffix_means(n_q, n_k, chunk):
+    # Q = 0: O_i is the mean of the first c_i = clip(i + n_k - n_q + 1, 0, n_k)
+    # V rows and L_i = ln c_i; a row with c_i = 0 gives O = 0, L = -inf.
+    d = 5
+    _, K, V, _ = _rand_head(n_q, n_k, d, seed=n_q * 3 + n_k)
+    r = oracle.attention_head(np.zeros((n_q, d)), K, V, causal="bottom_right", row_chunk=chunk)
+    cnt = _visible_counts(n_q, n_k, n_k - n_q)
+    live = cnt > 0
+    means = np.zeros((n_q, d))
+    means[live] = np.cumsum(V, axis=0)[cnt[live] - 1] / cnt[live, None]
+    np.testing.assert_allclose(r["O"], means, rtol=0, atol=1e-13)
+    assert np.all(np.isneginf(r["L"][~live]))
+    np.testing.assert_allclose(r["L"][live], np.log(cnt[live]), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(1, 9), (5, 40), (33, 70), (70, 70)])
+def test_bottom_right_is_the_tail_of_a_square_causal_problem(n_q, n_k):
+    # n_q <= n_k: the queries are the last n_q of an n_k-long sequence, so the
+    # result equals the last n_q rows of the square top-left causal problem
+    # (itself pinned to torch's sdpa above); with dO zero on the earlier rows
+    # the square problem's dK, dV are the bottom-right ones.
+    d = 6
+    Qf, K, V, dOf = _rand_head(n_k, n_k, d, seed=n_q + 2 * n_k)
+    dOf[: n_k - n_q] = 0.0
+    sq = oracle.attention_head(Qf, K, V, dOf, causal=True)
+    br = oracle.attention_head(Qf[n_k - n_q:], K, V, dOf[n_k - n_q:], causal="bottom_right")
+    tail = slice(n_k - n_q, None)
+    for key, want in (("O", sq["O"][tail]), ("L", sq["L"][tail]), ("dQ", sq["dQ"][tail]),
+                      ("dK", sq["dK"]), ("dV", sq["dV"])):
+        np.testing.assert_allclose(br[key], want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(5, 40), (33, 70), (16, 16), (1, 7)])
+def test_bottom_right_matches_torch_lower_right_bias(n_q, n_k):
+    # torch's causal_lower_right bias is an independent implementation of the
+    # same alignment (defined there for n_q <= n_k, where no row is empty).
+    from torch.nn.attention.bias import causal_lower_right
+    Q, K, V, dO = (torch.from_numpy(a) for a in _rand_head(n_q, n_k, 8, seed=n_q + n_k))
+    Qt, Kt, Vt = (a.clone().requires_grad_(True) for a in (Q, K, V))
+    bias = causal_lower_right(n_q, n_k)
+    ref = torch.nn.functional.scaled_dot_product_attention(Qt[None], Kt[None], Vt[None],
+                                                           attn_mask=bias)[0]
+    ref.backward(dO)
+    r = oracle.attention_head(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), causal="bottom_right")
+    np.testing.assert_allclose(r["O"], ref.detach().numpy(), rtol=0, atol=1e-13)
+    for name, t in (("dQ", Qt), ("dK", Kt), ("dV", Vt)):
+        np.testing.assert_allclose(r[name], t.grad.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_q,n_k,d", [(8, 5, 4), (6, 1, 2), (5, 8, 3), (8, 8, 4)])
+def test_bottom_right_finite_differences(n_q, n_k, d):
+    err = _fd_check(oracle.attention_head, n_q, n_k, d, "bottom_right", seed=n_q * 13 + n_k + d)
+    assert err < 1e-7, err
+
+
+def test_bottom_right_dead_rows():
+    # n_q > n_k: rows 0 .. n_q - n_k - 1 see no key. They give O = 0,
+    # L = -inf, dQ = 0, and the live rows are those of the problem without
+    # them (the dead rows add nothing to dK, dV).
+    n_q, n_k, d = 11, 4, 3
+    Q, K, V, dO = _rand_head(n_q, n_k, d, seed=31)
+    r = oracle.attention_head(Q, K, V, dO, causal="bottom_right")
+    dead = n_q - n_k
+    assert np.all(r["O"][:dead] == 0) and np.all(np.isneginf(r["L"][:dead]))
+    assert np.all(r["dQ"][:dead] == 0)
+    live = oracle.attention_head(Q[dead:], K, V, dO[dead:], causal="bottom_right")
+    for key in ("O", "L", "dQ"):
+        np.testing.assert_allclose(r[key][dead:], live[key], rtol=0, atol=1e-13)
+    for key in ("dK", "dV"):
+        np.testing.assert_allclose(r[key], live[key], rtol=0, atol=1e-13)
+
+
+def _bottom_right_pins_pass(fn):
+    """Compact bottom-right pins against an attention_head-like fn."""
+    ok = True
+    d = 4
+    for n_q, n_k in ((12, 9), (9, 12)):
+        _, K, V, _ = _rand_head(n_q, n_k, d, seed=41 + n_q)
+        r = fn(np.zeros((n_q, d)), K, V, causal="bottom_right", row_chunk=5)
+        cnt = _visible_counts(n_q, n_k, n_k - n_q)
+        live = cnt > 0
+        means = np.zeros((n_q, d))
+        means[live] = np.cumsum(V, 0)[cnt[live] - 1] / cnt[live, None]
+        with np.errstate(divide="ignore"):
+            want_l = np.where(live, np.log(np.maximum(cnt, 1)), -np.inf)
+        ok &= np.allclose(r["O"], means, atol=1e-12)
+        ok &= bool(np.array_equal(np.isneginf(r["L"]), ~live))
+        ok &= np.allclose(r["L"][live], want_l[live], atol=1e-12)
+    # tail of the square top-left problem (forward and backward)
+    Qf, K, V, dOf = _rand_head(10, 10, 3, seed=43)
+    dOf[:4] = 0.0
+    sq = oracle.attention_head(Qf, K, V, dOf, causal=True)
+    br = fn(Qf[4:], K, V, dOf[4:], causal="bottom_right")
+    for key, want in (("O", sq["O"][4:]), ("dQ", sq["dQ"][4:]), ("dK", sq["dK"]), ("dV", sq["dV"])):
+        ok &= np.allclose(br[key], want, atol=1e-10)
+    # torch's lower-right causal bias (independent), n_q < n_k
+    from torch.nn.attention.bias import causal_lower_right
+    Q, K, V, dO = (torch.from_numpy(a) for a in _rand_head(6, 11, 4, seed=45))
+    Qt, Kt, Vt = (a.clone().requires_grad_(True) for a in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Qt[None], Kt[None], Vt[None], attn_mask=causal_lower_right(6, 11))[0]
+    ref.backward(dO)
+    r = fn(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), causal="bottom_right")
+    for got, want in ((r["O"], ref.detach()), (r["dQ"], Qt.grad), (r["dK"], Kt.grad), (r["dV"], Vt.grad)):
+        ok &= np.allclose(got, want.numpy(), atol=1e-10)
+    # dead rows in the backward: zero dQ, finite everything
+    Q, K, V, dO = _rand_head(7, 3, 3, seed=44)
+    r = fn(Q, K, V, dO, causal="bottom_right")
+    ok &= bool(np.all(np.isfinite(r["dK"])) and np.all(np.isfinite(r["dV"])))
+    ok &= bool(np.all(r["dQ"][:4] == 0) and np.all(r["O"][:4] == 0))
+    return bool(ok)
+
+
+def test_bottom_right_pins_pass_on_the_oracle():
+    assert _bottom_right_pins_pass(oracle.attention_head)
+
+
+# --------------------------------------------------------------------------
 # planted mistakes: each one must trip at least one pin above
 # --------------------------------------------------------------------------
 
@@ -329,16 +473,22 @@ def test_pins_pass_on_the_oracle():
 def _mutant_scores(kind):
     orig = oracle_mod._scores
 
-    def scores(Qr, K, row_ids, causal, scale):
+    def scores(Qr, K, row_ids, off, scale):
         if kind == "mask_local_rows":      # causal mask indexed by chunk-local row
-            return orig(Qr, K, np.arange(len(row_ids)), causal, scale)
-        if kind == "mask_diagonal":        # hides the diagonal too (j >= i)
-            S = orig(Qr, K, row_ids, causal, scale)
-            if causal:
-                S[np.arange(K.shape[0])[None, :] == row_ids[:, None]] = -np.inf
+            return orig(Qr, K, np.arange(len(row_ids)), off, scale)
+        if kind == "mask_diagonal":        # hides the diagonal too (j >= i + off)
+            S = orig(Qr, K, row_ids, off, scale)
+            if off is not None:
+                S[np.arange(K.shape[0])[None, :] == row_ids[:, None] + off] = -np.inf
             return S
         if kind == "no_scale":
-            return orig(Qr, K, row_ids, causal, 1.0)
+            return orig(Qr, K, row_ids, off, 1.0)
+        if kind == "offset_ignored":       # bottom-right treated as top-left
+            return orig(Qr, K, row_ids, None if off is None else 0, scale)
+        if kind == "offset_sign":          # diagonal shifted the wrong way
+            return orig(Qr, K, row_ids, None if off is None else -off, scale)
+        if kind == "offset_plus_one":      # one key too many (j <= i + off + 1)
+            return orig(Qr, K, row_ids, None if off is None else off + 1, scale)
         raise ValueError(kind)
     return scores
 
@@ -347,6 +497,23 @@ def _mutant_scores(kind):
 def test_planted_score_mistakes_are_caught(kind, monkeypatch):
     monkeypatch.setattr(oracle_mod, "_scores", _mutant_scores(kind))
     assert not _pins_pass(oracle_mod.attention_head)
+
+
+@pytest.mark.parametrize("kind", ["mask_local_rows", "mask_diagonal", "no_scale",
+                                  "offset_ignored", "offset_sign", "offset_plus_one"])
+def test_planted_bottom_right_mistakes_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle_mod, "_scores", _mutant_scores(kind))
+    assert not _bottom_right_pins_pass(oracle_mod.attention_head)
+
+
+def test_planted_dead_row_mistakes_are_caught(monkeypatch):
+    # A row with no visible key must come out as O = 0, L = -inf, dQ = 0;
+    # plain three-pass softmax of such a row gives NaN instead.
+    def naive(X, scale=1.0):
+        P, m, l = oracle_mod.softmax_three_pass(np.asarray(X, dtype=np.float64) * scale)
+        return P, m + np.log(l)
+    monkeypatch.setattr(oracle_mod, "row_softmax", naive)
+    assert not _bottom_right_pins_pass(oracle_mod.attention_head)
 
 
 @pytest.mark.parametrize("kind", ["log2_L", "dQ_no_scale", "dK_no_scale", "D_dropped",
