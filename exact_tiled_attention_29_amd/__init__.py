@@ -21,7 +21,8 @@ import os
 import torch  # imported before libfa.so so the process shares torch's HIP runtime
 
 __all__ = [
-    "FA_BF16", "FA_F32", "FAError", "library_path", "load_library",
+    "FA_BF16", "FA_F32", "FA_NO_MASK", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT",
+    "FAError", "library_path", "load_library",
     "fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_row_softmax",
     "fa_status_str", "fa_abi_version",
     "forward", "backward", "row_softmax", "FlashAttention", "attention",
@@ -30,8 +31,14 @@ __all__ = [
 FA_BF16 = 0
 FA_F32 = 1
 
+# values of the `causal` argument
+FA_NO_MASK = 0
+FA_CAUSAL_TOP_LEFT = 1       # key j visible to query i iff j <= i
+FA_CAUSAL_BOTTOM_RIGHT = 2   # key j visible to query i iff j <= i + n_k - n_q
+
 _STATUS = {0: "FA_OK", 1: "FA_E_NULLPTR", 2: "FA_E_SHAPE", 3: "FA_E_DTYPE", 4: "FA_E_HEADDIM",
-           5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP"}
+           5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP", 8: "FA_E_CAUSAL"}
+_ABI_VERSION = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -72,7 +79,7 @@ def load_library():
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
     lib.fa_abi_version.restype = i32
-    if lib.fa_abi_version() != 1:
+    if lib.fa_abi_version() != _ABI_VERSION:
         raise RuntimeError("libfa.so ABI version mismatch")
     _lib = lib
     return lib
@@ -128,6 +135,18 @@ def _code(dtype: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {dtype}; expected bfloat16 or float32")
 
 
+def _mask_code(causal) -> int:
+    """The C `causal` value of False / True / "top_left" / "bottom_right"
+    (or the ints 0, 1, 2 themselves)."""
+    if isinstance(causal, str):
+        codes = {"none": FA_NO_MASK, "top_left": FA_CAUSAL_TOP_LEFT,
+                 "bottom_right": FA_CAUSAL_BOTTOM_RIGHT}
+        if causal not in codes:
+            raise ValueError(f"causal must be one of {sorted(codes)}, got {causal!r}")
+        return codes[causal]
+    return int(causal)
+
+
 def _check(t: torch.Tensor, name: str, shape, dtype=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
@@ -155,6 +174,10 @@ def _event_handle(e) -> int:
 def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None):
     """O, L = attention(q, k, v). q: [B,H,n_q,d]; k, v: [B,H,n_k,d].
 
+    causal: False, True (= "top_left": key j visible to query i iff j <= i)
+    or "bottom_right" (j <= i + n_k - n_q; a query that sees no key gets
+    O = 0, L = -inf).
+
     o_dtype defaults to the input dtype; torch.float32 gives the unrounded
     fp32 O for bf16 inputs. Returns (O, L) with L fp32 [B,H,n_q].
     """
@@ -174,7 +197,7 @@ def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None)
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
     _check(lse, "lse", (B, H, n_q), torch.float32)
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _code(o_dtype),
-                lse.data_ptr(), B, H, n_q, n_k, d, dt, causal, scale, _stream(q.device))
+                lse.data_ptr(), B, H, n_q, n_k, d, dt, _mask_code(causal), scale, _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_fwd")
     return out, lse
@@ -197,7 +220,8 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
     _check(do, "do", (B, H, n_q, d), q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = fa_bwd_workspace_bytes(B, H, n_q, n_k, d, dt, causal)
+    mask = _mask_code(causal)
+    need = fa_bwd_workspace_bytes(B, H, n_q, n_k, d, dt, mask)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if grads is None:
@@ -210,7 +234,7 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
         ev = (ctypes.c_void_p * 4)(*[_event_handle(e) for e in events])
     st = fa_bwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _code(o.dtype),
                       lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      B, H, n_q, n_k, d, dt, causal, scale, workspace.data_ptr(), workspace.numel(),
+                      B, H, n_q, n_k, d, dt, mask, scale, workspace.data_ptr(), workspace.numel(),
                       _stream(q.device), ev)
     if st != 0:
         raise FAError(st, "fa_bwd")

@@ -22,7 +22,9 @@ bool dim_ok(int d, int dtype) {
 // Shared checks of the forward and backward calls. Sets *empty when there
 // is nothing to compute for the query side (batch, heads or n_q is zero).
 int check_common(int batch, int heads, int n_q, int n_k, int d, int dtype, int o_dtype,
-                 float scale, bool* empty) {
+                 int causal, float scale, bool* empty) {
+    if (causal != FA_NO_MASK && causal != FA_CAUSAL_TOP_LEFT && causal != FA_CAUSAL_BOTTOM_RIGHT)
+        return FA_E_CAUSAL;
     if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_DTYPE;
     if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_E_DTYPE;
     if (dtype == FA_F32 && o_dtype != FA_F32) return FA_E_DTYPE;
@@ -32,8 +34,11 @@ int check_common(int batch, int heads, int n_q, int n_k, int d, int dtype, int o
     const long long bh = (long long)batch * heads;
     if (bh > 0x7fffffffLL) return FA_E_SHAPE;
     // Every element offset must fit in 63 bits and the per-row grids in 31.
-    const long long rows = bh * (long long)(n_q > n_k ? n_q : n_k);
+    const long long n_max = n_q > n_k ? n_q : n_k;
+    const long long rows = bh * n_max;
     if (rows > (1LL << 40)) return FA_E_SHAPE;
+    // One head's Q, K or V is addressed with 32-bit byte offsets.
+    if (n_max * d * (dtype == FA_BF16 ? 2 : 4) > 0x7fffffffLL) return FA_E_SHAPE;
     *empty = bh == 0 || n_q == 0;
     if (!(*empty) && n_k == 0) return FA_E_SHAPE;
     return FA_OK;
@@ -48,11 +53,16 @@ size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
 
+// Diagonal of the causal mask: key j is visible to query i iff j <= i + offset.
+int causal_offset(int causal, int n_q, int n_k) {
+    return causal == FA_CAUSAL_BOTTOM_RIGHT ? n_k - n_q : 0;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fa_abi_version(void) { return 1; }
+int fa_abi_version(void) { return 2; }
 
 const char* fa_status_str(int status) {
     switch (status) {
@@ -64,6 +74,7 @@ const char* fa_status_str(int status) {
         case FA_E_SCALE: return "scale must be finite and > 0";
         case FA_E_WORKSPACE: return "workspace missing or too small";
         case FA_E_HIP: return "HIP runtime error";
+        case FA_E_CAUSAL: return "causal must be 0, 1 or 2";
         default: return "unknown status";
     }
 }
@@ -72,23 +83,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, fl
            int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
            void* stream) {
     bool empty = false;
-    int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, scale, &empty);
+    int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, scale, &empty);
     if (st != FA_OK) return st;
     if (empty) return FA_OK;
     if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
     fa::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.bh = batch * heads; a.n_q = n_q; a.n_k = n_k; a.d = d;
-    a.causal = causal != 0; a.o_f32 = o_dtype == FA_F32; a.scale = scale;
+    a.causal = causal != FA_NO_MASK; a.coff = causal_offset(causal, n_q, n_k);
+    a.o_f32 = o_dtype == FA_F32; a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
     return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
 }
 
 size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int dtype, int causal) {
-    (void)causal;
     bool empty = false;
     const int o_dtype = dtype == FA_F32 ? FA_F32 : FA_BF16;
-    if (check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, 1.0f, &empty) != FA_OK) return 0;
+    if (check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, 1.0f, &empty) != FA_OK) return 0;
     if (empty) return 0;
     return workspace_bytes((long long)batch * heads, n_q, d, dtype);
 }
@@ -99,7 +110,7 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int
                  void* workspace, size_t workspace_bytes_given, void* stream,
                  void* const* events) {
     bool empty = false;
-    int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, scale, &empty);
+    int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, scale, &empty);
     if (st != FA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     const long long bh = (long long)batch * heads;
@@ -120,7 +131,8 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.d_o = d_o;
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.bh = (int)bh; a.n_q = n_q; a.n_k = n_k; a.d = d;
-    a.causal = causal != 0; a.o_f32 = o_dtype == FA_F32; a.scale = scale;
+    a.causal = causal != FA_NO_MASK; a.coff = causal_offset(causal, n_q, n_k);
+    a.o_f32 = o_dtype == FA_F32; a.scale = scale;
     a.events = (hipEvent_t const*)events;
     char* w = (char*)workspace;
     a.drow = (float*)w;

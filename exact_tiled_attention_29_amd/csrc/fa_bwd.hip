@@ -5,12 +5,16 @@
 // saved logsumexp as exp(S - L); dV += P^T dO; dP = dO V^T; dS = P * (dP - D)
 // with D = rowsum(dO * O); dQ += scale * dS K; dK += scale * dS^T Q. Tiles
 // wholly in the causal future are skipped. The derivative rules are those of
-// page 3 ("Flash Attention"), section 1.5.
+// page 3 ("Flash Attention"), section 1.5. The causal diagonal is a runtime
+// offset coff (key j visible to query i iff j <= i + coff), as in the forward;
+// a query row that sees no key (L = -inf) gets L2 = +inf, so its P, dS and
+// dQ are 0 and it adds nothing to dK, dV.
 //
 // Three kernels on one stream:
 //  1. bwd_pre:  D = rowsum(dO * O) and L2 = L * log2(e) into per-head arrays
-//     padded to a multiple of 32 rows (padding: L2 = +inf, D = 0, so padded
-//     query rows get P = 0 and dS = 0 without any masking);
+//     padded to a multiple of 32 rows (padding and rows with L = -inf:
+//     L2 = +inf, D = 0, so those query rows get P = 0 and dS = 0 without any
+//     masking);
 //  2. bwd_dkdv: key-stationary. One workgroup per 128 keys of one (batch,
 //     head); each of its 4 waves keeps 32 keys' K and V rows in registers as
 //     MFMA operands and their dK, dV in fp32 accumulators, and walks the
@@ -71,8 +75,10 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
     if (prow < rows_pad && sub == 0) {
-        dp[prow] = valid ? acc : 0.0f;
-        l2p[prow] = valid ? Lse[(size_t)bh * n_q + q] * kLog2e : __builtin_huge_valf();
+        const float lse = valid ? Lse[(size_t)bh * n_q + q] : kNegInf;
+        const bool live = lse > kNegInf;
+        dp[prow] = live ? acc : 0.0f;
+        l2p[prow] = live ? lse * kLog2e : __builtin_huge_valf();
     }
 }
 
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
     bf16* __restrict__ dK, bf16* __restrict__ dV,
-    int n_q, int n_k, int n_q_pad, int n_ktiles, float scale, float scale2) {
+    int n_q, int n_k, int coff, int n_q_pad, int n_ktiles, float scale, float scale2) {
     constexpr int BKV = 128;           // keys per workgroup
     constexpr int KK = D / 16;
     constexpr int NDB = D / 32;
@@ -380,7 +386,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     };
 
     const int nqt = (n_q + kBQ - 1) / kBQ;
-    const int t_begin = CAUSAL ? k0 / kBQ : 0;
+    // first query tile with a row that sees key k0 (rows >= k0 - coff)
+    const int t_begin = CAUSAL ? max(0, k0 - coff) / kBQ : 0;
     auto noop = [](int) {};
     const std::integral_constant<int, 0> nv0{};
     auto none = []() {};
@@ -393,8 +400,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     // q0 + 4g is masked iff below lim), hand the fp32 values to wave B
     // through slot Sd and keep them as bf16 A operands for dV.
     auto finish_p = [&](int q0, float* p, bf16* Sd, bf16x8* pa) {
-        if ((kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0)) {
-            const int lim = key >= n_k ? 64 : (CAUSAL ? key - q0 - 4 * g : -1);
+        if ((kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0 + coff)) {
+            const int lim = key >= n_k ? 64 : (CAUSAL ? key - coff - q0 - 4 * g : -1);
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 if (8 * (v >> 2) + (v & 3) < lim) p[v] = 0.0f;
@@ -512,7 +519,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
-    bf16* __restrict__ dQ, int n_q, int n_k, int n_q_pad, int n_qtiles, float scale, float scale2) {
+    bf16* __restrict__ dQ, int n_q, int n_k, int coff, int n_q_pad, int n_qtiles, float scale,
+    float scale2) {
     constexpr int RW = 32;               // query rows per wave
     constexpr int BR = 4 * RW;           // query rows per workgroup
     constexpr int KK = D / 16;
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int v = 0; v < 16; ++v) neg_d[v] = -drw;
 
     int kend = n_k;
-    if (CAUSAL) kend = min(n_k, min(q0 + BR, n_q));
+    if (CAUSAL) kend = max(0, min(n_k, min(q0 + BR, n_q) + coff));
     const int ntiles = (kend + kBC - 1) / kBC;
 
     // K, V tiles straight to LDS; rows past n_k read as zeros (masked keys).
@@ -630,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     };
 
     auto tile_step = [&](const bf16* Kb, const bf16* Vb, int ks) {
-        const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row);
+        const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row + coff);
         if (!active) return;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
@@ -638,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(troff[db][h]));
-        const bool need_mask = (ks + kBC > n_k) || (CAUSAL && ks + kBC - 1 > qw);
+        const bool need_mask = (ks + kBC > n_k) || (CAUSAL && ks + kBC - 1 > qw + coff);
         // Two 32-key halves, one after the other, to keep fewer values live.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 dsb[v >> 3][v & 7] = to_bf16(p * dpt[v]);
             }
             if (need_mask)
-                apply_mask((CAUSAL ? min(n_k, row + 1) : n_k) - ks - 32 * kb - 4 * g, dsb);
+                apply_mask((CAUSAL ? min(n_k, row + 1 + coff) : n_k) - ks - 32 * kb - 4 * g, dsb);
             // dQ^T (d x queries) += K^T dS^T; K^T operands by transpose reads.
             mfma_priority(true);
 #pragma unroll
@@ -738,14 +746,14 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * n_ktiles)), dim3(kPairThreads), 0,
                        st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o,
                        (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dk, (bf16*)a.dv,
-                       a.n_q, a.n_k, n_q_pad, n_ktiles, a.scale, a.scale * kLog2e);
+                       a.n_q, a.n_k, a.coff, n_q_pad, n_ktiles, a.scale, a.scale * kLog2e);
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 2, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * n_qtiles)), dim3(kThreads), 0,
                        st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o,
                        (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dq,
-                       a.n_q, a.n_k, n_q_pad, n_qtiles, a.scale, a.scale * kLog2e);
+                       a.n_q, a.n_k, a.coff, n_q_pad, n_qtiles, a.scale, a.scale * kLog2e);
     e = hipGetLastError();
     return e == hipSuccess ? record_stage(a, 3, st) : e;
 }

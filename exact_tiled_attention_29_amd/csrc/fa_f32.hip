@@ -7,6 +7,9 @@
 // (dK, dV) and keeps it in registers; key/query tiles of 32 rows are staged
 // in LDS and read as broadcasts. The backward's dQ comes from its own pass
 // over the key tiles, so no atomics are needed and results are deterministic.
+// The causal diagonal is a runtime offset coff (key j visible to query i iff
+// j <= i + coff); a row that sees no key gets O = 0, L = -inf and zero dQ,
+// and adds nothing to dK, dV.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -32,7 +35,8 @@ __device__ __forceinline__ void stage_rows(float* dst, const float* src, int row
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ Lse, int n_q, int n_k, int n_qtiles, float scale2) {
+    float* __restrict__ O, float* __restrict__ Lse, int n_q, int n_k, int coff, int n_qtiles,
+    float scale2) {
     __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
     const int tid = threadIdx.x;
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
     }
     float m = kNegInf, l = 0.0f;
     int kend = n_k;
-    if (CAUSAL) kend = min(n_k, min(q0 + kRows, n_q));
+    if (CAUSAL) kend = max(0, min(n_k, min(q0 + kRows, n_q) + coff));
     for (int ks = 0; ks < kend; ks += kTile) {
         __syncthreads();
         stage_rows<D>(Ks, Kh, ks, n_k, tid);
@@ -64,7 +68,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
 #pragma unroll
             for (int d = 0; d < D; ++d) acc = fmaf(q[d], Ks[j * D + d], acc);
             const int key = ks + j;
-            if (key >= n_k || (CAUSAL && key > row)) acc = kNegInf;
+            if (key >= n_k || (CAUSAL && key > row + coff)) acc = kNegInf;
             s[j] = acc;
             mx = fmaxf(mx, acc);
         }
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
         m = m_new;
     }
     if (row < n_q) {
-        const float inv = 1.0f / l;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;   // no visible key: O = 0, L = -inf
 #pragma unroll
         for (int d = 0; d < D; ++d) O[((size_t)bh * n_q + row) * D + d] = o[d] * inv;
         Lse[(size_t)bh * n_q + row] = kLn2 * (m + fast_log2(l));
@@ -113,8 +117,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ drow,
-    float* __restrict__ dK, float* __restrict__ dV, int n_q, int n_k, int n_ktiles, float scale,
-    float scale2) {
+    float* __restrict__ dK, float* __restrict__ dV, int n_q, int n_k, int coff, int n_ktiles,
+    float scale, float scale2) {
     __shared__ __attribute__((aligned(16))) float Qs[kTile * D];
     __shared__ __attribute__((aligned(16))) float dOs[kTile * D];
     __shared__ float Ls[kTile], Ds[kTile];
@@ -132,14 +136,15 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
         vr[d] = key < n_k ? V[((size_t)bh * n_k + key) * D + d] : 0.0f;
         dk[d] = dv[d] = 0.0f;
     }
-    const int qbeg = CAUSAL ? (k0 / kTile) * kTile : 0;
+    const int qbeg = CAUSAL ? (max(0, k0 - coff) / kTile) * kTile : 0;  // rows >= k0 - coff
     for (int qs = qbeg; qs < n_q; qs += kTile) {
         __syncthreads();
         stage_rows<D>(Qs, Qh, qs, n_q, tid);
         stage_rows<D>(dOs, dOh, qs, n_q, tid);
         if (tid < kTile) {
             const int q = qs + tid;
-            Ls[tid] = q < n_q ? Lse[(size_t)bh * n_q + q] * kLog2e : __builtin_huge_valf();
+            const float lse = q < n_q ? Lse[(size_t)bh * n_q + q] : kNegInf;
+            Ls[tid] = lse > kNegInf ? lse * kLog2e : __builtin_huge_valf();   // P = 0 if no key
             Ds[tid] = q < n_q ? drow[(size_t)bh * n_q + q] : 0.0f;
         }
         __syncthreads();
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
                 dp = fmaf(dOs[i * D + d], vr[d], dp);
             }
             float p = fast_exp2(s - Ls[i]);
-            if (q >= n_q || (CAUSAL && key > q)) p = 0.0f;
+            if (q >= n_q || (CAUSAL && key > q + coff)) p = 0.0f;
             const float ds = p * (dp - Ds[i]);
 #pragma unroll
             for (int d = 0; d < D; ++d) {
@@ -177,7 +182,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ drow,
-    float* __restrict__ dQ, int n_q, int n_k, int n_qtiles, float scale, float scale2) {
+    float* __restrict__ dQ, int n_q, int n_k, int coff, int n_qtiles, float scale, float scale2) {
     __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
     const int tid = threadIdx.x;
@@ -194,10 +199,11 @@ __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
         dor[d] = row < n_q ? dO[((size_t)bh * n_q + row) * D + d] : 0.0f;
         dq[d] = 0.0f;
     }
-    const float l2 = row < n_q ? Lse[(size_t)bh * n_q + row] * kLog2e : 0.0f;
+    const float lse = row < n_q ? Lse[(size_t)bh * n_q + row] : kNegInf;
+    const float l2 = lse > kNegInf ? lse * kLog2e : __builtin_huge_valf();   // P = 0 if no key
     const float Dr = row < n_q ? drow[(size_t)bh * n_q + row] : 0.0f;
     int kend = n_k;
-    if (CAUSAL) kend = min(n_k, min(q0 + kRows, n_q));
+    if (CAUSAL) kend = max(0, min(n_k, min(q0 + kRows, n_q) + coff));
     for (int ks = 0; ks < kend; ks += kTile) {
         __syncthreads();
         stage_rows<D>(Ks, Kh, ks, n_k, tid);
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
                 dp = fmaf(dor[d], Vs[j * D + d], dp);
             }
             float p = fast_exp2(s - l2);
-            if (key >= n_k || (CAUSAL && key > row)) p = 0.0f;
+            if (key >= n_k || (CAUSAL && key > row + coff)) p = 0.0f;
             const float ds = p * (dp - Dr);
 #pragma unroll
             for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, Ks[j * D + d], dq[d]);
@@ -234,7 +240,7 @@ hipError_t fwd_launch(const FwdArgs& a, hipStream_t st) {
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kRows), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                       a.n_q, a.n_k, nt, a.scale * kLog2e);
+                       a.n_q, a.n_k, a.coff, nt, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -255,14 +261,14 @@ hipError_t bwd_launch(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkt)), dim3(kRows), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.d_o,
-                       a.lse, a.drow, (float*)a.dk, (float*)a.dv, a.n_q, a.n_k, nkt, a.scale,
+                       a.lse, a.drow, (float*)a.dk, (float*)a.dv, a.n_q, a.n_k, a.coff, nkt, a.scale,
                        a.scale * kLog2e);
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 2, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqt)), dim3(kRows), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.d_o,
-                       a.lse, a.drow, (float*)a.dq, a.n_q, a.n_k, nqt, a.scale, a.scale * kLog2e);
+                       a.lse, a.drow, (float*)a.dq, a.n_q, a.n_k, a.coff, nqt, a.scale, a.scale * kLog2e);
     e = hipGetLastError();
     return e == hipSuccess ? record_stage(a, 3, st) : e;
 }

@@ -5,7 +5,10 @@
 // tile, walk the key tiles left to right keeping a running max m and running
 // sum l per row; rescale the output accumulator by exp(m_old - m_new); finish
 // with O / l and L = m + log(l). Key tiles that lie wholly in the causal
-// future are skipped (same section). The running-statistics recurrence is
+// future are skipped (same section). The causal diagonal is a runtime offset
+// coff (key j visible to query i iff j <= i + coff): 0 is the pages' top-left
+// mask, n_k - n_q the bottom-right one, under which a query may see no key
+// at all; such a row gets O = 0 and L = -inf. The running-statistics recurrence is
 // the one of page 1, section 1 and page 3 ("Flash Attention"), section 1.1.
 //
 // MI355X mapping (not from the pages):
@@ -37,7 +40,7 @@ template <int D, bool CAUSAL, bool OF32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ Lse,
-    int n_q, int n_k, int n_qtiles, float scale2) {
+    int n_q, int n_k, int coff, int n_qtiles, float scale2) {
     constexpr int RW = 32;               // query rows per wave
     constexpr int BR = 4 * RW;           // query rows per workgroup
     constexpr int KK = D / 16;           // MFMA k-steps over d
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 
     int kend = n_k;
-    if (CAUSAL) kend = min(n_k, min(q0 + BR, n_q));  // keys <= last row of the tile
+    if (CAUSAL) kend = max(0, min(n_k, min(q0 + BR, n_q) + coff));  // keys <= last row + coff
     const int ntiles = (kend + kBC - 1) / kBC;
 
     // K and V tiles go straight from global memory to LDS (no registers),
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     // Compute on one staged tile (K rows in Kb, V rows in Vb).
     auto tile_step = [&](const bf16* Kb, const bf16* Vb, int ks) {
-        const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row);
+        const bool active = wave_last_row >= qw && (!CAUSAL || ks <= wave_last_row + coff);
         if (active) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
@@ -179,9 +182,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             // Mask keys past n_k and (causal) keys after the query: the key of
             // element v is ks + 32*kb + 4g + 8*(v/4) + v%4, so one compare of a
             // constant against a per-lane limit decides it.
-            const bool need_mask = (ks + kBC > n_k) || (CAUSAL && ks + kBC - 1 > qw);
+            const bool need_mask = (ks + kBC > n_k) || (CAUSAL && ks + kBC - 1 > qw + coff);
             if (need_mask) {
-                const int lim = (CAUSAL ? min(n_k, qw + r + 1) : n_k) - ks - 4 * g;
+                const int lim = (CAUSAL ? min(n_k, qw + r + 1 + coff) : n_k) - ks - 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -246,11 +249,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         copies_barrier();
     }
 
-    // Epilogue: O / l, L = ln 2 * (m + log2 l).
+    // Epilogue: O / l, L = ln 2 * (m + log2 l). A row that saw no key has
+    // l = 0 and m = -inf: O = 0 and L = -inf.
     const float l = halves_sum(l_run);
     const int row = qw + r;
     if (row < n_q) {
-        const float inv = 1.0f / l;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
         const size_t obase = ((size_t)bh * n_q + row) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -279,7 +283,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OF32>), dim3((unsigned)nwg), dim3(kThreads), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o, a.lse,
-                       a.n_q, a.n_k, n_qtiles, a.scale * kLog2e);
+                       a.n_q, a.n_k, a.coff, n_qtiles, a.scale * kLog2e);
     return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ struct FwdArgs {
     int bh;  // batch * heads
     int n_q, n_k, d;
     bool causal;
+    int coff;    // causal diagonal: key j visible to query i iff j <= i + coff
     bool o_f32;  // O stored as float32 (else bf16)
     float scale;
 };
@@ -33,6 +34,7 @@ struct BwdArgs {
     int bh;
     int n_q, n_k, d;
     bool causal;
+    int coff;    // as in FwdArgs
     bool o_f32;
     float scale;
     float* drow;    // fp32 D = rowsum(dO * O): [bh, n_q] (fp32 path) or [bh, n_q_pad] (bf16)

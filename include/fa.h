@@ -17,8 +17,10 @@
  *
  * Supported: dtype FA_BF16 with d in {64, 128}; dtype FA_F32 with d in
  * {16, 32, 64, 128}. n_k >= 1 whenever there is work (a softmax over zero
- * keys is undefined). batch, heads or n_q equal to 0 is an empty call: the
- * forward does nothing; the backward zeroes dK and dV when n_q == 0.
+ * keys is undefined). One head's Q, K or V must be under 2 GiB
+ * (max(n_q, n_k) * d * element size < 2^31), else FA_E_SHAPE. batch, heads
+ * or n_q equal to 0 is an empty call: the forward does nothing; the backward
+ * zeroes dK and dV when n_q == 0.
  */
 #ifndef FA_H
 #define FA_H
@@ -42,8 +44,16 @@ typedef enum {
     FA_E_HEADDIM = 4,   /* d not supported for this dtype                      */
     FA_E_SCALE = 5,     /* scale not finite or not > 0                         */
     FA_E_WORKSPACE = 6, /* backward workspace NULL or smaller than required    */
-    FA_E_HIP = 7        /* a HIP launch or runtime call failed                 */
+    FA_E_HIP = 7,       /* a HIP launch or runtime call failed                 */
+    FA_E_CAUSAL = 8     /* causal is not one of the fa_mask values             */
 } fa_status;
+
+/* The `causal` argument of fa_fwd / fa_bwd. */
+typedef enum {
+    FA_NO_MASK = 0,             /* every key visible                            */
+    FA_CAUSAL_TOP_LEFT = 1,     /* key j visible to query i iff j <= i          */
+    FA_CAUSAL_BOTTOM_RIGHT = 2  /* key j visible to query i iff j <= i + n_k - n_q */
+} fa_mask;
 
 /*
  * Forward pass: O = softmax(scale * Q K^T [+ causal mask]) V and
@@ -62,9 +72,17 @@ typedef enum {
  *                                 round-to-nearest-even rounding of the fp32
  *                                 result.
  * lse    [B,H,n_q] float32, natural-log logsumexp L.
- * causal 0: every key visible. 1: key j visible to query i iff j <= i
- *        (top-left aligned, also when n_q != n_k: page 1, section 2,
- *        standard_attention masks the strict upper triangle).
+  * causal FA_NO_MASK (0): every key visible.
+ *        FA_CAUSAL_TOP_LEFT (1): key j visible to query i iff j <= i, also
+ *        when n_q != n_k (page 1, section 2, standard_attention masks the
+ *        strict upper triangle).
+ *        FA_CAUSAL_BOTTOM_RIGHT (2): key j visible to query i iff
+ *        j <= i + n_k - n_q, so the last query sees every key (queries are
+ *        the newest n_q positions of an n_k-long sequence; not on the pages,
+ *        which define only the top-left mask). Same as 1 when n_q == n_k.
+ *        When n_q > n_k the first n_q - n_k queries see no key: their O is
+ *        0 and their L is -inf.
+ *        Any other value: FA_E_CAUSAL.
  * scale  multiplies Q K^T; the usual value is 1/sqrt(d). Finite, > 0.
  * Outputs are written for every row < n_q and nothing else is written.
  */
@@ -94,7 +112,8 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
  * Attention", section 1.5, the derivatives of O = PV and of P = softmax(S)).
  *
  * o, lse are the outputs of fa_fwd for the same q, k, v, causal and scale
- * (o in o_dtype). d_o [B,H,n_q,d] dtype. dq [B,H,n_q,d], dk, dv [B,H,n_k,d]
+ * (o in o_dtype). A query row with no visible key (L = -inf, bottom-right
+ * mask with n_q > n_k) gets dQ = 0 and adds nothing to dK or dV. d_o [B,H,n_q,d] dtype. dq [B,H,n_q,d], dk, dv [B,H,n_k,d]
  * in dtype; every element is overwritten.
  * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
  * 256-byte aligned, owned by the caller, contents on entry ignored. Calls
@@ -151,7 +170,7 @@ int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float sca
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (2 added FA_CAUSAL_BOTTOM_RIGHT and FA_E_CAUSAL). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

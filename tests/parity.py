@@ -10,6 +10,8 @@ When an exact gradient is identically zero (a single key: every softmax row
 is the constant 1, so dQ = dK = 0), "max|reference|" is floored at 1e-3 of
 the largest reference gradient of the three, so the bar stays relative to
 the gradients' scale instead of collapsing to 0.
+A query row that sees no key (bottom-right mask, n_q > n_k) must come out
+exactly as the oracle defines it: O = 0, L = -inf, dQ = 0.
 """
 from __future__ import annotations
 
@@ -63,8 +65,17 @@ def check_heads(res, q, k, v, do, causal, dtype, heads, scale=None, grads=True, 
         ridx = slice(None) if rows is None else rows
         cidx = slice(None) if cols is None else cols
         o_key = "O32" if dtype == "bf16" else "O"
-        e_o = np.abs(f64(res[o_key][b, h])[ridx] - ref["O"]).max()
-        e_l = np.abs(f64(res["L"][b, h])[ridx] - ref["L"]).max()
+        got_o = f64(res[o_key][b, h])[ridx]
+        got_l = f64(res["L"][b, h])[ridx]
+        dead = np.isneginf(ref["L"])
+        if dead.any():
+            assert np.all(np.isneginf(got_l[dead])), f"{tag} head {(b, h)}: L of an empty row != -inf"
+            assert np.all(got_o[dead] == 0), f"{tag} head {(b, h)}: O of an empty row != 0"
+            if grads:
+                assert np.all(f64(res["dQ"][b, h])[ridx][dead] == 0), \
+                    f"{tag} head {(b, h)}: dQ of an empty row != 0"
+        e_o = np.abs(got_o - ref["O"]).max()
+        e_l = np.abs(got_l[~dead] - ref["L"][~dead]).max() if (~dead).any() else 0.0
         worst["O"] = max(worst.get("O", 0.0), e_o)
         worst["L"] = max(worst.get("L", 0.0), e_l)
         assert e_o <= tol["O"], f"{tag} head {(b, h)}: max|dO| {e_o:.3e} > {tol['O']}"

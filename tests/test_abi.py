@@ -17,7 +17,7 @@ import exact_tiled_attention_29_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULLPTR, SHAPE, DTYPE, HEADDIM, SCALE, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
+OK, NULLPTR, SHAPE, DTYPE, HEADDIM, SCALE, WORKSPACE, HIP, CAUSAL = 0, 1, 2, 3, 4, 5, 6, 7, 8
 BF16, F32 = 0, 1
 P = 0x1000  # a non-null dummy pointer; never dereferenced on the validation paths
 
@@ -51,8 +51,8 @@ def test_library_exports_every_header_function(lib):
 
 
 def test_status_strings(lib):
-    assert lib.fa_abi_version() == 1
-    for code in range(8):
+    assert lib.fa_abi_version() == 2
+    for code in range(9):
         s = fa.fa_status_str(code)
         assert s and s != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
@@ -92,6 +92,16 @@ def test_validation_codes(lib, call):
     assert call(q=None) == NULLPTR
     assert call(v=None) == NULLPTR
     assert call(lse=None) == NULLPTR
+    # causal: 0 none, 1 top-left, 2 bottom-right; anything else is refused
+    for bad in (3, -1, 255):
+        assert call(causal=bad) == CAUSAL
+    for good in (1, 2):
+        assert call(causal=good, q=None) == NULLPTR   # accepted, then the pointer check
+    # one head's Q, K or V must stay under 2 GiB (32-bit byte offsets)
+    assert call(n_q=1 << 23, n_k=8, d=128) == SHAPE
+    assert call(n_k=1 << 23, d=128) == SHAPE
+    assert call(n_k=(1 << 23) - 1, d=128, q=None) == NULLPTR
+    assert call(dtype=F32, o_dtype=F32, n_k=1 << 22, d=128) == SHAPE
 
 
 def test_backward_specific_codes(lib):
@@ -121,6 +131,18 @@ def test_workspace_bytes(lib):
     assert fa.fa_bwd_workspace_bytes(B, H, 0, n_k, d, BF16, 0) == 0
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 96, BF16, 0) == 0
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, 0, d, BF16, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 2) == 2 * up(B * H * pad * 4)
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 3) == 0
+
+
+def test_mask_codes_of_the_binding():
+    assert fa._mask_code(False) == fa.FA_NO_MASK == 0
+    assert fa._mask_code(True) == fa.FA_CAUSAL_TOP_LEFT == 1
+    assert fa._mask_code("top_left") == 1
+    assert fa._mask_code("bottom_right") == fa.FA_CAUSAL_BOTTOM_RIGHT == 2
+    assert fa._mask_code("none") == 0
+    with pytest.raises(ValueError):
+        fa._mask_code("lower_right")
 
 
 def rows_call(**kw):

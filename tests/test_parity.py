@@ -118,7 +118,27 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", EDGE)
+# bottom-right aligned mask (key j visible to query i iff j <= i + n_k - n_q):
+# the offset not a multiple of any tile, a single decoding query, rows and
+# whole workgroups that see no key (n_q > n_k), and offsets larger than a tile
+EDGE_BR = [
+    (1, 2, 50, 130, 32, "f32", "bottom_right"),
+    (1, 2, 130, 50, 32, "f32", "bottom_right"),
+    (1, 1, 65, 190, 128, "f32", "bottom_right"),
+    (2, 2, 96, 160, 64, "f32", "bottom_right"),
+    (1, 2, 1, 300, 64, "bf16", "bottom_right"),
+    (1, 2, 1, 300, 128, "bf16", "bottom_right"),
+    (1, 2, 300, 1, 64, "bf16", "bottom_right"),
+    (1, 3, 200, 333, 64, "bf16", "bottom_right"),
+    (1, 3, 333, 200, 64, "bf16", "bottom_right"),
+    (1, 2, 128, 1100, 128, "bf16", "bottom_right"),
+    (1, 2, 1100, 128, 128, "bf16", "bottom_right"),
+    (2, 2, 257, 1000, 128, "bf16", "bottom_right"),
+    (1, 2, 700, 613, 128, "bf16", "bottom_right"),
+]
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", EDGE + EDGE_BR)
 def test_edge_shapes(B, H, n_q, n_k, d, dtype, causal):
     w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
     q, k, v, do = make_inputs(w, seed=n_q * 7 + n_k)
@@ -152,6 +172,52 @@ def test_zero_query_gives_mean_of_values(dtype):
     tol = 1e-2 if dtype == "bf16" else 1e-5
     assert np.abs(f64(res["O32"]) - want).max() < tol
     assert np.abs(f64(res["L"]) - np.log(cnt)[None, None]).max() < (1e-3 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_q,n_k", [(150, 100), (90, 230)])
+def test_bottom_right_zero_query_gives_prefix_means(dtype, n_q, n_k):
+    # Q = 0: query i averages the first c_i = clip(i + n_k - n_q + 1, 0, n_k)
+    # value rows, L_i = ln c_i; rows with c_i = 0 give O = 0, L = -inf.
+    w = workloads.custom(1, 2, n_q, n_k, 64, dtype, "bottom_right")
+    _, k, v, do = make_inputs(w, seed=4)
+    q = torch.zeros(1, 2, n_q, 64, dtype=k.dtype)
+    res = run(q, k, v, do, "bottom_right")
+    cnt = np.clip(np.arange(n_q) + n_k - n_q + 1, 0, n_k)
+    live = cnt > 0
+    want = np.zeros((1, 2, n_q, 64))
+    want[:, :, live] = np.cumsum(f64(v), axis=2)[:, :, cnt[live] - 1] / cnt[live][None, None, :, None]
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    got = f64(res["O32"])
+    assert np.abs(got - want).max() < tol
+    assert np.all(got[:, :, ~live] == 0)
+    lg = f64(res["L"])
+    assert np.all(np.isneginf(lg[:, :, ~live]))
+    assert np.abs(lg[:, :, live] - np.log(cnt[live])).max() < (1e-3 if dtype == "bf16" else 1e-5)
+    assert np.all(f64(res["dQ"])[:, :, ~live] == 0)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 32)])
+def test_bottom_right_square_is_top_left(dtype, d):
+    # With n_q == n_k the two alignments are the same mask: bitwise equal.
+    w = workloads.custom(1, 3, 777, 777, d, dtype, True)
+    q, k, v, do = make_inputs(w, seed=5)
+    a = run(q, k, v, do, True)
+    b = run(q, k, v, do, "bottom_right")
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_bottom_right_new_queries_against_long_context():
+    # 512 new queries against 8192 cached keys (d = 128): query i sees keys
+    # 0 .. 7680 + i. Every head compared in full, plus the sum invariants.
+    w = workloads.custom(1, 4, 512, 8192, 128, "bf16", "bottom_right")
+    q, k, v, do = make_inputs(w, seed=6)
+    res = run(q, k, v, do, "bottom_right")
+    worst = check_heads(res, q, k, v, do, "bottom_right", "bf16", [(0, h) for h in range(4)],
+                        tag="bottom_right 512x8192")
+    print(worst)
+    check_sum_invariants(res, do, "bf16", "bottom_right 512x8192")
 
 
 def test_empty_calls():

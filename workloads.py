@@ -29,7 +29,7 @@ class Workload:
     n_k: int
     d: int
     dtype: str          # "bf16" or "f32"
-    causal: bool
+    causal: bool | str  # False, True (top-left mask) or "bottom_right"
     q_std: float = 1.0
 
     def shape_q(self):
