@@ -14,8 +14,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool dim_ok(int d, int dtype) {
-    if (dtype == FA_BF16) return d == 64 || d == 128;
-    if (dtype == FA_F32) return d == 16 || d == 32 || d == 64 || d == 128;
+    if (dtype == FA_BF16) return d == 32 || d == 64 || d == 96 || d == 128 || d == 256;
+    if (dtype == FA_F32) return d == 16 || d == 32 || d == 64 || d == 96 || d == 128;
     return false;
 }
 

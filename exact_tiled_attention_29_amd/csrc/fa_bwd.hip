@@ -43,12 +43,21 @@ constexpr int kBC = 64;   // keys per tile of the dQ kernel
 // --------------------------------------------------------------------------
 // 1. D = rowsum(dO * O) and L2 = L * log2(e), padded per head.
 // --------------------------------------------------------------------------
+// Lanes that share one row of the row pass: the largest power of two (at
+// most 16) that divides the row's D/8 chunks of 8 elements.
+constexpr int pre_lanes_per_row(int chunks) {
+    int l = 1;
+    while (l < 16 && chunks % (2 * l) == 0) l *= 2;
+    return l;
+}
+
 template <int D, typename OT>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
     const OT* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ Lse,
     float* __restrict__ l2p, float* __restrict__ dp, long long rows_pad, int n_q, int n_q_pad) {
-    constexpr int LPR = D / 8;               // lanes per row, 8 elements each
-    constexpr int RPB = kThreads / LPR;      // rows per block
+    constexpr int LPR = pre_lanes_per_row(D / 8);  // lanes per row
+    constexpr int CPL = D / 8 / LPR;               // chunks of 8 elements per lane
+    constexpr int RPB = kThreads / LPR;            // rows per block
     const int tid = threadIdx.x;
     const long long prow = (long long)blockIdx.x * RPB + tid / LPR;
     const int sub = tid % LPR;
@@ -57,20 +66,23 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
     const bool valid = prow < rows_pad && q < n_q;
     float acc = 0.0f;
     if (valid) {
-        const size_t base = ((size_t)bh * n_q + q) * D + 8 * sub;
-        const bf16x8 dov = *(const bf16x8*)(dO + base);
-        float ov[8];
-        if constexpr (sizeof(OT) == 4) {
-            const float4 a = *(const float4*)(O + base), b = *(const float4*)(O + base + 4);
-            ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
-            ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
-        } else {
-            const bf16x8 x = *(const bf16x8*)(O + base);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ov[i] = bf2f(x[i]);
+        for (int c = 0; c < CPL; ++c) {
+            const size_t base = ((size_t)bh * n_q + q) * D + 8 * (sub + LPR * c);
+            const bf16x8 dov = *(const bf16x8*)(dO + base);
+            float ov[8];
+            if constexpr (sizeof(OT) == 4) {
+                const float4 a = *(const float4*)(O + base), b = *(const float4*)(O + base + 4);
+                ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
+                ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
+            } else {
+                const bf16x8 x = *(const bf16x8*)(O + base);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ov[i] = bf2f(x[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = fmaf(bf2f(dov[i]), ov[i], acc);
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf(bf2f(dov[i]), ov[i], acc);
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
@@ -85,44 +97,51 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 // --------------------------------------------------------------------------
 // 2. dK, dV: key-stationary, two waves per group of keys.
 // --------------------------------------------------------------------------
-// One workgroup of 8 waves per 128 keys of one (batch, head), as four groups
-// of 32 keys. A group is handled by a pair of waves that share its work:
-//   wave A (waves 0-3) keeps the group's K rows as MFMA operands and the dV
-//     accumulator: S = Q K^T, P = exp2(S * scale * log2(e) - L2),
+// One workgroup of 2 * NP waves per 32 * NP keys of one (batch, head), as NP
+// groups of 32 keys (NP = 4; NP = 2 at d = 256, where a wave needs more than
+// 256 registers, so only one wave may share each SIMD). A group is handled
+// by a pair of waves that share its work:
+//   wave A (waves 0 .. NP-1) keeps the group's K rows as MFMA operands and
+//     the dV accumulator: S = Q K^T, P = exp2(S * scale * log2(e) - L2),
 //     dV += P^T dO;
-//   wave B (waves 4-7) keeps the group's V rows and the dK accumulator:
+//   wave B (waves NP .. 2NP-1) keeps the group's V rows and the dK accumulator:
 //     dP = dO V^T, dS = P * (dP - D), dK += dS^T Q.
 // Wave A hands P (fp32, in the accumulator layout both waves use) to wave B
 // through LDS. Splitting the group this way halves each wave's registers,
-// so two waves share each SIMD and one issues while the other waits.
+// so (for NP = 4) two waves share each SIMD and one issues while the other
+// waits.
 // Query tiles of 32 rows stream through a ring of three LDS slots; a slot
 // also holds the P that wave A computed from its tile, which wave B uses one
 // step later. Within a step each wave overlaps its VALU work (A: the softmax
 // of this tile; B: dS of the previous one) with its MFMAs.
-constexpr int kPairThreads = 512;
+// Wave pairs per dK/dV workgroup.
+template <int D>
+constexpr int dkdv_pairs() { return D >= 256 ? 2 : 4; }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
+template <int D, bool CAUSAL, int NP>
+__global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
     bf16* __restrict__ dK, bf16* __restrict__ dV,
     int n_q, int n_k, int coff, int n_q_pad, int n_ktiles, float scale, float scale2) {
-    constexpr int BKV = 128;           // keys per workgroup
+    constexpr int NW = 2 * NP;         // waves
+    constexpr int BKV = 32 * NP;       // keys per workgroup
     constexpr int KK = D / 16;
     constexpr int NDB = D / 32;
     constexpr int NJ = 2 * NDB;        // (c, db) products of a dV or dK update
     constexpr int TILE = kBQ * D;      // elements per Q or dO tile
     constexpr int NCH = TILE * 2 / 1024;  // 1 KB copies per tensor and tile
-    constexpr int CPW = 2 * NCH / 8;      // copies per wave and tile
-    static_assert(CPW * 8 == 2 * NCH, "copies split evenly over the waves");
+    static_assert(NCH * 1024 == TILE * 2, "whole 1 KB copies");
+    constexpr int CPW = (2 * NCH + NW - 1) / NW;   // copies per wave and tile (at most)
+    constexpr bool kEvenCopies = 2 * NCH % NW == 0;
     constexpr int XW = 64 * 16;        // fp32 words of P per wave pair
 
     // One LDS object per ring slot: Q tile, dO tile (row-major, swizzled
-    // 16-byte chunks), L2 and D of the tile's rows, and the four pairs' P
+    // 16-byte chunks), L2 and D of the tile's rows, and the NP pairs' P
     // (at byte 2 * (2 * TILE + 4 * kBQ); see exoff below).
     // Distinct objects let the compiler tell a slot being copied from slots
     // being read (it tracks only a few copy targets).
-    constexpr int SLOT = 2 * TILE + 4 * kBQ + 8 * XW;   // bf16 units
+    constexpr int SLOT = 2 * TILE + 4 * kBQ + 2 * NP * XW;   // bf16 units
     __shared__ __attribute__((aligned(16))) bf16 Sl0[SLOT];
     __shared__ __attribute__((aligned(16))) bf16 Sl1[SLOT];
     __shared__ __attribute__((aligned(16))) bf16 Sl2[SLOT];
@@ -134,8 +153,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
-    const bool role_a = wave < 4;
-    const int pair = wave & 3;
+    const bool role_a = wave < NP;
+    const int pair = wave & (NP - 1);
 
     int bh, kt;   // rank = key tile, ascending: longest causal work first
     work_item(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, &bh, &kt);
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     // Copy query tile t (rows q0 .. q0+31; rows past n_q fall outside the
     // buffer and read as zeros, and their L2 = +inf padding makes P = 0) and
     // its L2, D values into a slot. Copy b of the tile (Q chunks, then dO
-    // chunks) is issued by wave b % 8.
+    // chunks) is issued by wave b % NW.
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, n_q * D * 2);
     const __amdgpu_buffer_rsrc_t dors = make_rsrc(dOh, n_q * D * 2);
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(l2h, n_q_pad * 4);
@@ -178,7 +197,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
         const int q0 = t * kBQ;
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-            const int b = 8 * i + wave;
+            const int b = NW * i + wave;
+            if (!kEvenCopies && b >= 2 * NCH) break;
             const bool is_q = b < NCH;
             const int chunk = is_q ? b : b - NCH;
             const int p = 64 * chunk + lane;
@@ -261,7 +281,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
             acc_s = mfma32(a[kk % (kLookS + 1)], kv[kk], acc_s);
             extra(kk);
         }
-        __builtin_amdgcn_sched_group_barrier(kDsRead, kLookS, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, kLookS < KK ? kLookS : KK, 0);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
@@ -294,7 +314,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
             acc[j % NDB] = mfma32(xa[j / NDB], b[j % (kLookG + 1)], acc[j % NDB]);
             extra(j);
         }
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * kLookG, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * (kLookG < NJ ? kLookG : NJ), 0);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
@@ -392,7 +412,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const std::integral_constant<int, 0> nv0{};
     auto none = []() {};
     // VALU instructions per MFMA of wave A's softmax (fma, exp per element).
-    const std::integral_constant<int, 2 * (16 / NJ)> nv_softmax{};
+    // Softmax elements per product of the dV update (the last product may
+    // get fewer when NJ does not divide 16).
+    constexpr int EPM = (16 + NJ - 1) / NJ;
+    const std::integral_constant<int, 2 * EPM> nv_softmax{};
     const std::integral_constant<int, 4> n_row_reads{};
 
     // Wave A's P of tile t (q0 = t * kBQ): zero where the key is past n_k or
@@ -440,13 +463,12 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
                 launder_offsets();
                 float lq[16], p[16];
                 f32x16 s;
-                constexpr int EPM = 16 / NJ;
                 stream(q_of(Sc), s, do_of(Sp), pa_p, [&]() { read_rows(Sc, 0, lq); }, n_row_reads,
                        noop, nv0, [&](int j) {
 #pragma unroll
                     for (int e = 0; e < EPM; ++e) {
                         const int v = EPM * j + e;
-                        p[v] = fast_exp2(fmaf(s[v], scale2, -lq[v]));
+                        if (v < 16) p[v] = fast_exp2(fmaf(s[v], scale2, -lq[v]));
                     }
                 }, nv_softmax);
                 finish_p(t * kBQ, p, Sc, pa_p);
@@ -516,7 +538,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
 // 3. dQ: query-stationary.
 // --------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
     bf16* __restrict__ dQ, int n_q, int n_k, int coff, int n_q_pad, int n_qtiles, float scale,
@@ -723,9 +745,10 @@ template <int D, bool CAUSAL>
 hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     const int n_q_pad = dq_rows_padded(a.n_q);
     const long long rows_pad = (long long)a.bh * n_q_pad;
-    constexpr int RPB = kThreads / (D / 8);
+    constexpr int RPB = kThreads / pre_lanes_per_row(D / 8);   // as in bwd_pre_kernel
     const long long nb = (rows_pad + RPB - 1) / RPB;
-    const int n_ktiles = (a.n_k + 127) / 128;
+    constexpr int NP = dkdv_pairs<D>();
+    const int n_ktiles = (a.n_k + 32 * NP - 1) / (32 * NP);
     const int n_qtiles = (a.n_q + 127) / 128;
     if (nb > 0x7fffffffLL || (long long)a.bh * n_ktiles > 0x7fffffffLL ||
         (long long)a.bh * n_qtiles > 0x7fffffffLL)
@@ -743,7 +766,7 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 1, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * n_ktiles)), dim3(kPairThreads), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NP>), dim3((unsigned)(a.bh * n_ktiles)), dim3(128 * NP), 0,
                        st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o,
                        (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dk, (bf16*)a.dv,
                        a.n_q, a.n_k, a.coff, n_q_pad, n_ktiles, a.scale, a.scale * kLog2e);
@@ -777,8 +800,11 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
     switch (a.d) {
+        case 32: return a.causal ? launch_kernels<32, true>(a, st) : launch_kernels<32, false>(a, st);
         case 64: return a.causal ? launch_kernels<64, true>(a, st) : launch_kernels<64, false>(a, st);
+        case 96: return a.causal ? launch_kernels<96, true>(a, st) : launch_kernels<96, false>(a, st);
         case 128: return a.causal ? launch_kernels<128, true>(a, st) : launch_kernels<128, false>(a, st);
+        case 256: return a.causal ? launch_kernels<256, true>(a, st) : launch_kernels<256, false>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -121,15 +121,28 @@ __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
 
 // XOR swizzle of the 16-byte chunks of a row-major bf16 tile with rows of D
 // elements (D/8 chunks): row rho keeps logical chunk c at physical chunk
-// c ^ tile_swz<D>(rho). Chosen so that (a) 16 consecutive rows read at one
-// logical chunk (an MFMA operand read with ds_read_b128) hit 16 different
-// bank groups, and (b) 4 consecutive rows (aligned to 4) read over 4
-// consecutive chunks (a transpose read) hit disjoint banks.
+// c ^ tile_swz<D>(rho). The LDS has 64 banks of 4 bytes, i.e. 16 groups of
+// 16 bytes; chunk k of the tile sits in group k % 16. Chosen so that (a) 16
+// consecutive rows read at one logical chunk (an MFMA operand read with
+// ds_read_b128) hit 16 different groups, and (b) 4 consecutive rows (aligned
+// to 4) read over an aligned quad of chunks (a transpose read) hit disjoint
+// groups. The swizzle only permutes chunks within aligned quads (values
+// < 4) or aligned groups of 16 (values < 16, for rows of 16 or 32 chunks),
+// so every physical chunk stays inside its row.
+//  D = 128, 256 (16 or 32 chunks a row): the row's own offset is a multiple
+//    of 16 groups, so the swizzle alone spreads rows: 4*(rho%4) separates
+//    the 4 rows of a quad, (rho/4)%4 the 4 quads of 16 rows.
+//  D = 64 (8 chunks): two rows share the 16 groups; 4*((rho/2)%2) separates
+//    them, (rho/4)%4 the quads.
+//  D = 32, 96 (4 or 12 chunks): the row offsets 4*rho or 12*rho mod 16
+//    already take the 4 multiples of 4 over a quad of rows, so only the
+//    quads of 16 rows need separating: (rho/4)%4.
 template <int D>
 __host__ __device__ constexpr int tile_swz(int rho) {
-    static_assert(D == 64 || D == 128, "head dim");
-    if constexpr (D == 128) return (4 * (rho & 3)) ^ ((rho >> 2) & 3);
-    else return (4 * ((rho >> 1) & 1)) ^ ((rho >> 2) & 3);
+    static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dim");
+    if constexpr (D == 128 || D == 256) return (4 * (rho & 3)) ^ ((rho >> 2) & 3);
+    else if constexpr (D == 64) return (4 * ((rho >> 1) & 1)) ^ ((rho >> 2) & 3);
+    else return (rho >> 2) & 3;
 }
 
 // Element offset of (row, col) in a swizzled row-major tile.

@@ -289,6 +289,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
         case 16: return fwd_d<16>(a, st);
         case 32: return fwd_d<32>(a, st);
         case 64: return fwd_d<64>(a, st);
+        case 96: return fwd_d<96>(a, st);
         case 128: return fwd_d<128>(a, st);
         default: return hipErrorInvalidValue;
     }
@@ -299,6 +300,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
         case 16: return bwd_d<16>(a, st);
         case 32: return bwd_d<32>(a, st);
         case 64: return bwd_d<64>(a, st);
+        case 96: return bwd_d<96>(a, st);
         case 128: return bwd_d<128>(a, st);
         default: return hipErrorInvalidValue;
     }

@@ -13,7 +13,8 @@
 //
 // MI355X mapping (not from the pages):
 //  * one workgroup = 4 waves = 128 query rows of one (batch, head), two
-//    workgroups per CU; each wave owns 32 rows and keeps its Q rows in
+//    workgroups per CU (one at d = 256, where the wave needs more than 256
+//    registers and the K/V buffers take 128 KB of LDS); each wave owns 32 rows and keeps its Q rows in
 //    registers as the B operand of S^T = K Q^T, so every per-row quantity
 //    (m, l, the O accumulator column) lives in one lane pair (l, l^32);
 //  * K and V tiles (64 keys, row-major, swizzled 16-byte chunks) are copied
@@ -37,7 +38,7 @@ constexpr int kThreads = 256;
 constexpr int kBC = 64;  // keys per tile
 
 template <int D, bool CAUSAL, bool OF32>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ Lse,
     int n_q, int n_k, int coff, int n_qtiles, float scale2) {
@@ -300,8 +301,11 @@ int fwd_bf16_rows_per_wg(const FwdArgs&) { return 128; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
     switch (a.d) {
+        case 32: return dispatch_mask<32>(a, st);
         case 64: return dispatch_mask<64>(a, st);
+        case 96: return dispatch_mask<96>(a, st);
         case 128: return dispatch_mask<128>(a, st);
+        case 256: return dispatch_mask<256>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

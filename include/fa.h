@@ -15,8 +15,8 @@
  * is returned. A failed launch returns FA_E_HIP. Calls are asynchronous: a
  * fault inside a kernel surfaces at the caller's next synchronisation.
  *
- * Supported: dtype FA_BF16 with d in {64, 128}; dtype FA_F32 with d in
- * {16, 32, 64, 128}. n_k >= 1 whenever there is work (a softmax over zero
+ * Supported: dtype FA_BF16 with d in {32, 64, 96, 128, 256}; dtype FA_F32
+ * with d in {16, 32, 64, 96, 128}. n_k >= 1 whenever there is work (a softmax over zero
  * keys is undefined). One head's Q, K or V must be under 2 GiB
  * (max(n_q, n_k) * d * element size < 2^31), else FA_E_SHAPE. batch, heads
  * or n_q equal to 0 is an empty call: the forward does nothing; the backward

@@ -82,9 +82,14 @@ def test_validation_codes(lib, call):
     assert call(n_q=-3) == SHAPE
     assert call(n_k=0) == SHAPE
     assert call(heads=1 << 20, batch=1 << 12) == SHAPE
-    assert call(d=32) == HEADDIM          # bf16 supports 64 and 128
-    assert call(d=96) == HEADDIM
-    assert call(dtype=F32, o_dtype=F32, d=48) == HEADDIM
+    for d in (0, 16, 48, 80, 112, 160, 192, 512):   # bf16: 32, 64, 96, 128, 256
+        assert call(d=d) == HEADDIM, d
+    for d in (32, 64, 96, 128, 256):
+        assert call(d=d, q=None) == NULLPTR, d
+    for d in (8, 48, 256):                          # f32: 16, 32, 64, 96, 128
+        assert call(dtype=F32, o_dtype=F32, d=d) == HEADDIM, d
+    for d in (16, 32, 64, 96, 128):
+        assert call(dtype=F32, o_dtype=F32, d=d, q=None) == NULLPTR, d
     assert call(scale=0.0) == SCALE
     assert call(scale=-1.0) == SCALE
     assert call(scale=float("inf")) == SCALE
@@ -129,7 +134,8 @@ def test_workspace_bytes(lib):
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 1) == 2 * up(B * H * pad * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 32, F32, 0) == up(rows * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, 0, n_k, d, BF16, 0) == 0
-    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 96, BF16, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 80, BF16, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 96, BF16, 0) == 2 * up(B * H * pad * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, 0, d, BF16, 0) == 0
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 2) == 2 * up(B * H * pad * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 3) == 0

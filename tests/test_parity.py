@@ -138,7 +138,27 @@ EDGE_BR = [
 ]
 
 
-@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", EDGE + EDGE_BR)
+# head dims beyond 64 / 128: bf16 32, 96, 256 (d = 256 runs the 4-wave dK/dV
+# variant and one workgroup per CU), fp32 96
+EDGE_DIMS = [
+    (1, 1, 1, 1, 32, "bf16", False),
+    (1, 2, 200, 333, 32, "bf16", True),
+    (1, 2, 333, 200, 32, "bf16", False),
+    (1, 2, 81, 130, 32, "bf16", "bottom_right"),
+    (2, 2, 257, 257, 96, "bf16", True),
+    (1, 3, 190, 450, 96, "bf16", False),
+    (1, 2, 81, 130, 96, "bf16", "bottom_right"),
+    (1, 1, 1, 1, 256, "bf16", True),
+    (1, 2, 300, 300, 256, "bf16", True),
+    (1, 2, 129, 65, 256, "bf16", False),
+    (1, 2, 200, 517, 256, "bf16", "bottom_right"),
+    (1, 2, 517, 200, 256, "bf16", "bottom_right"),
+    (1, 2, 140, 70, 96, "f32", True),
+    (1, 1, 100, 100, 96, "f32", "bottom_right"),
+]
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", EDGE + EDGE_BR + EDGE_DIMS)
 def test_edge_shapes(B, H, n_q, n_k, d, dtype, causal):
     w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
     q, k, v, do = make_inputs(w, seed=n_q * 7 + n_k)
@@ -218,6 +238,18 @@ def test_bottom_right_new_queries_against_long_context():
                         tag="bottom_right 512x8192")
     print(worst)
     check_sum_invariants(res, do, "bf16", "bottom_right 512x8192")
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_head_dims_at_scale(d):
+    # 2048 x 2048 causal per head, every query tile and key group busy;
+    # two heads compared in full, the sum invariants on all four.
+    w = workloads.custom(1, 4, 2048, 2048, d, "bf16", True)
+    q, k, v, do = make_inputs(w, seed=d)
+    res = run(q, k, v, do, True)
+    worst = check_heads(res, q, k, v, do, True, "bf16", [(0, 0), (0, 3)], tag=f"d={d} n=2048")
+    print(d, worst)
+    check_sum_invariants(res, do, "bf16", f"d={d} n=2048")
 
 
 def test_empty_calls():
