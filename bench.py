@@ -212,6 +212,11 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--shape", default=None, metavar="BxHxNQxNKxD",
+                    help="time a bf16 shape of your own instead of a named workload (not the "
+                         "headline metric)")
+    ap.add_argument("--mask", default="top_left", choices=["none", "top_left", "bottom_right"],
+                    help="mask of --shape")
     ap.add_argument("--cpu-heads", type=int, default=10, help="heads the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -250,8 +255,15 @@ def main():
     if args.rows:
         return bench_rows(args)
 
-    name = args.workload or workloads.HEADLINE
-    w = workloads.WORKLOADS[name]
+    if args.shape:
+        B, H, NQ, NK, D = (int(x) for x in args.shape.lower().split("x"))
+        causal = {"none": False, "top_left": True, "bottom_right": "bottom_right"}[args.mask]
+        w = workloads.custom(B, H, NQ, NK, D, "bf16", causal,
+                             name=f"b{B}h{H}_q{NQ}_k{NK}_d{D}_{args.mask}")
+    else:
+        w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+    metric = METRIC if w.name == workloads.HEADLINE else \
+        f"attention TFLOP/s fwd+bwd ({w.dtype}, mask {w.causal}, n_q={w.n_q}, n_k={w.n_k}, d={w.d})"
     fa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -265,7 +277,8 @@ def main():
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
     ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.d,
                                                       fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32,
-                                                      w.causal)), dtype=torch.uint8, device=dev)
+                                                      fa._mask_code(w.causal))),
+                     dtype=torch.uint8, device=dev)
 
     if args.copy_mib:
         a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -335,7 +348,7 @@ def main():
         log(f"[bench]   {kname:15s} {t:.4f} ms")
 
     result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": metric, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, workloads.py)",

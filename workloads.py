@@ -43,9 +43,18 @@ class Workload:
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
 
     def fwd_flop(self) -> float:
-        """4 * n_q * n_k * d per (batch, head), halved when causal."""
-        f = 4.0 * self.n_q * self.n_k * self.d * self.batch * self.heads
-        return f * 0.5 if self.causal else f
+        """4 * d FLOP per visible (query, key) pair and (batch, head): 4 n_q
+        n_k d unmasked; halved for a causal mask over a square problem (the
+        usual convention); the exact visible-pair count for a causal mask
+        with n_q != n_k."""
+        per_pair = 4.0 * self.d * self.batch * self.heads
+        if not self.causal:
+            return per_pair * self.n_q * self.n_k
+        if self.n_q == self.n_k:
+            return per_pair * self.n_q * self.n_k * 0.5
+        off = self.n_k - self.n_q if self.causal == "bottom_right" else 0
+        visible = sum(min(max(i + off + 1, 0), self.n_k) for i in range(self.n_q))
+        return per_pair * visible
 
     def fwd_bwd_flop(self) -> float:
         """Backward counted as 2.5x forward, so fwd+bwd is 3.5x forward."""
