@@ -110,6 +110,31 @@ def summarize_stats(stats_dir, out_path, command):
     print("\n".join(lines))
 
 
+def summarize_counters(dirs, out_path, command):
+    """Average per dispatch of every counter (raw or derived) found in the
+    rocprofv3 --pmc output directories, one row per kernel."""
+    acc = {}
+    for d in dirs:
+        for r in _read_counter_csv(d):
+            key = (r.get("Kernel_Name", ""), r.get("Counter_Name", ""))
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    kernels = sorted({k for k, _ in acc})
+    counters = sorted({c for _, c in acc})
+    lines = [f"command: {command}", f"source_hash {kernel_source_hash()}",
+             "values: average per kernel dispatch (derived counters as rocprofv3 defines them)"]
+    for k in kernels:
+        if not any((k, c) in acc for c in counters):
+            continue
+        lines.append(f"kernel {k[:100]!r}")
+        for c in counters:
+            if (k, c) in acc:
+                v = acc[(k, c)]
+                lines.append(f"  {c:32s} {sum(v) / len(v):.6g}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_from_summary(kernel_key):
     """HBM bytes per launch of the kernel, or None when no summary exists or
     the kernels changed since the counters were taken."""
@@ -227,6 +252,8 @@ def main():
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="average every counter of rocprofv3 --pmc runs per kernel dispatch")
     ap.add_argument("--summary-out", default=PMC_SUMMARY)
     ap.add_argument("--summary-copy-mib", type=int, default=512)
     ap.add_argument("--summary-command", default="", help="command line recorded in a summary")
@@ -243,6 +270,9 @@ def main():
         return 0
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.summary_out, args.summary_command)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.summary_out, args.summary_command)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
