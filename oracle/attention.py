@@ -151,7 +151,9 @@ def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=N
 
     With a subset of rows only those rows are computed when dO is None. The
     backward needs every query row for dK and dV, so with dO given all rows
-    are visited and only the requested ones are kept.
+    are visited and only the requested ones are kept, unless cols is empty:
+    then only the requested rows are visited (their O, L and dQ need no
+    other row).
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -173,7 +175,8 @@ def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=N
         dQ = np.zeros((len(rows), d))
         dK = np.zeros((len(cols), d))
         dV = np.zeros((len(cols), d))
-        visit = np.arange(n_q)          # every row contributes to dK, dV
+        # every row contributes to dK, dV; only the requested ones to dQ
+        visit = np.arange(n_q) if len(cols) else np.unique(rows)
     else:
         visit = np.unique(rows)
 

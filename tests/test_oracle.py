@@ -261,6 +261,12 @@ def test_chunking_and_sampling_are_exact(causal):
         np.testing.assert_allclose(s[key], full[key][idx], rtol=0, atol=1e-13)
     f = oracle.attention_head(Q, K, V, causal=causal, rows=rows)
     np.testing.assert_allclose(f["O"], full["O"][rows], rtol=0, atol=1e-13)
+    # no key columns requested: only the requested rows are visited
+    q = oracle.attention_head(Q, K, V, dO, causal=causal, rows=rows, cols=np.array([], dtype=np.int64),
+                              row_chunk=3)
+    for key in ("O", "L", "dQ"):
+        np.testing.assert_allclose(q[key], full[key][rows], rtol=0, atol=1e-13)
+    assert q["dK"].shape == (0, 8) and q["dV"].shape == (0, 8)
 
 
 def test_batched_wrappers_match_heads():

@@ -78,6 +78,33 @@ def test_long_b1h8_n32768_d128_causal():
     check_sum_invariants(res, do, "bf16", w.name)
 
 
+def test_very_long_context_256k():
+    # 262144 tokens, one head, d = 128, causal (per-head tensors of 64 MB):
+    # O, L and dQ on sampled rows (the oracle visits only those rows), dK and
+    # dV on every key through the sum invariants.
+    n = 262144
+    w = workloads.custom(1, 1, n, n, 128, "bf16", True)
+    q, k, v, do = make_inputs(w, seed=7)
+    res = run(q, k, v, do, True)
+    edge = [0, 1, 127, 128, 65535, 65536, 131071, 131072, n - 129, n - 1]
+    rows = np.unique(np.concatenate([edge, np.random.default_rng(1).integers(0, n, 22)]))
+    worst = check_heads(res, q, k, v, do, True, "bf16", [(0, 0)], rows=rows,
+                        cols=np.array([], dtype=np.int64), tag="n=262144")
+    print(worst)
+    check_sum_invariants(res, do, "bf16", "n=262144")
+
+
+def test_million_token_forward():
+    # 2^20 tokens, one head, d = 64, causal, forward only: sampled rows.
+    n = 1 << 20
+    w = workloads.custom(1, 1, n, n, 64, "bf16", True)
+    q, k, v, do = make_inputs(w, seed=8)
+    res = run(q, k, v, do, True, backward=False)
+    edge = [0, 1, 4095, 4096, 524287, 524288, n - 1]
+    rows = np.unique(np.concatenate([edge, np.random.default_rng(2).integers(0, n, 9)]))
+    check_heads(res, q, k, v, do, True, "bf16", [(0, 0)], grads=False, rows=rows, tag="n=2^20 fwd")
+
+
 def test_long_forward_only_rows_all_heads():
     # Forward-only at 32K: sampled rows of every head.
     w = WORKLOADS["long_b1h8_n32768_d128_causal"]
