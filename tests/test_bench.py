@@ -1,0 +1,107 @@
+"""Host-side tests of bench.py and workloads.py (no GPU needed): the
+single-GPU guard, the rocprofv3 summary readers, the traffic lookup and the
+FLOP convention."""
+import csv
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _write_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_summarize_pmc_scales_by_the_copy_kernel(tmp_path):
+    mib = 1 << 20
+    # the copy of 512 MiB reads as half its bytes on FETCH_SIZE, exactly on WRITE_SIZE
+    fetch = [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "FETCH_SIZE", "Counter_Value": 512 * 1024 / 2},
+             {"Kernel_Name": "fwd_bf16_kernel", "Counter_Name": "FETCH_SIZE", "Counter_Value": 1000.0},
+             {"Kernel_Name": "fwd_bf16_kernel", "Counter_Name": "FETCH_SIZE", "Counter_Value": 3000.0}]
+    write = [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "WRITE_SIZE", "Counter_Value": 512 * 1024},
+             {"Kernel_Name": "fwd_bf16_kernel", "Counter_Name": "WRITE_SIZE", "Counter_Value": 500.0}]
+    _write_csv(str(tmp_path / "f" / "run_counter_collection.csv"), fetch)
+    _write_csv(str(tmp_path / "w" / "run_counter_collection.csv"), write)
+    out = tmp_path / "summary.txt"
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), 512 * mib, str(out), "cmd")
+    text = out.read_text().splitlines()
+    assert text[0] == "command: cmd"
+    assert text[1] == f"source_hash {bench.kernel_source_hash()}"
+    assert "fetch_scale 2.0000 write_scale 1.0000" in text[2]
+    line = next(l for l in text if "fwd_bf16_kernel" in l)
+    parts = line.split()
+    # average 2000 KiB per dispatch, scaled by 2: 4096000 bytes; write 500 KiB
+    assert float(parts[parts.index("fetch_bytes") + 1]) == 2000 * 1024 * 2
+    assert float(parts[parts.index("write_bytes") + 1]) == 500 * 1024
+
+
+def test_traffic_lookup_needs_matching_sources(tmp_path, monkeypatch):
+    summ = tmp_path / "hbm.txt"
+    summ.write_text("command: x\nsource_hash {}\ncopy_bytes 1 fetch_scale 2 write_scale 1\n"
+                    "kernel 'k_bwd_dkdv_kernel' fetch_bytes 100 write_bytes 20\n".format(bench.kernel_source_hash()))
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(summ))
+    assert bench.traffic_from_summary("bwd_dkdv") == 120.0
+    assert bench.traffic_from_summary("nothing_like_it") is None
+    summ.write_text(summ.read_text().replace(bench.kernel_source_hash(), "0000000000000000"))
+    assert bench.traffic_from_summary("bwd_dkdv") is None
+
+
+def test_summarize_stats_and_counters(tmp_path):
+    stats = [{"Name": "bwd_dkdv_kernel", "Calls": "3", "TotalDurationNs": "3000000", "AverageNs": "1000000",
+              "MinNs": "900000", "MaxNs": "1100000", "Percentage": "75.0"},
+             {"Name": "fwd_bf16_kernel", "Calls": "3", "TotalDurationNs": "1000000", "AverageNs": "333333",
+              "MinNs": "300000", "MaxNs": "400000", "Percentage": "25.0"}]
+    _write_csv(str(tmp_path / "s" / "run_kernel_stats.csv"), stats)
+    out = tmp_path / "stats.txt"
+    bench.summarize_stats(str(tmp_path / "s"), str(out), "cmd")
+    lines = out.read_text().splitlines()
+    assert lines[3].startswith("bwd_dkdv_kernel") and "1000.00" in lines[3]
+    cnt = [{"Kernel_Name": "fwd_bf16_kernel", "Counter_Name": "MfmaUtil", "Counter_Value": 40.0},
+           {"Kernel_Name": "fwd_bf16_kernel", "Counter_Name": "MfmaUtil", "Counter_Value": 60.0}]
+    _write_csv(str(tmp_path / "c" / "run_counter_collection.csv"), cnt)
+    out2 = tmp_path / "cnt.txt"
+    bench.summarize_counters([str(tmp_path / "c")], str(out2), "cmd")
+    body = out2.read_text()
+    assert "MfmaUtil" in body and " 50" in body
+
+
+@pytest.mark.parametrize("n_q,n_k,causal", [(37, 37, True), (50, 130, True), (130, 50, True),
+                                            (50, 130, "bottom_right"), (130, 50, "bottom_right"),
+                                            (64, 64, False), (1, 9, "bottom_right")])
+def test_forward_flop_convention(n_q, n_k, causal):
+    w = workloads.custom(2, 3, n_q, n_k, 16, "bf16", causal)
+    per_pair = 4 * 16 * 2 * 3
+    if not causal:
+        want = per_pair * n_q * n_k
+    elif n_q == n_k:
+        want = per_pair * n_q * n_k / 2          # the usual convention for square causal
+    else:
+        off = n_k - n_q if causal == "bottom_right" else 0
+        want = per_pair * np.clip(np.arange(n_q) + off + 1, 0, n_k).sum()
+    assert w.fwd_flop() == want
+    assert w.fwd_bwd_flop() == 3.5 * want
+
+
+def test_headline_workload_flops():
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    assert (w.batch, w.heads, w.n_q, w.n_k, w.d, w.dtype, w.causal) == (2, 32, 4096, 4096, 128, "bf16", True)
+    assert w.fwd_flop() == 4 * 4096 * 4096 * 128 * 64 / 2
