@@ -106,8 +106,10 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 //     dV += P^T dO;
 //   wave B (waves NP .. 2NP-1) keeps the group's V rows and the dK accumulator:
 //     dP = dO V^T, dS = P * (dP - D), dK += dS^T Q.
-// Wave A hands P (fp32, in the accumulator layout both waves use) to wave B
-// through LDS. Splitting the group this way halves each wave's registers,
+// Wave A hands P to wave B through LDS as the bf16 values it feeds its own
+// dV product (in the accumulator layout both waves use), so dS is formed
+// from the same rounded P; dS is rounded to bf16 for the dK product anyway.
+// Splitting the group this way halves each wave's registers,
 // so (for NP = 4) two waves share each SIMD and one issues while the other
 // waits.
 // Query tiles of 32 rows stream through a ring of three LDS slots; a slot
@@ -134,14 +136,14 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     static_assert(NCH * 1024 == TILE * 2, "whole 1 KB copies");
     constexpr int CPW = (2 * NCH + NW - 1) / NW;   // copies per wave and tile (at most)
     constexpr bool kEvenCopies = 2 * NCH % NW == 0;
-    constexpr int XW = 64 * 16;        // fp32 words of P per wave pair
+    constexpr int XB = 64 * 16 * 2;    // bytes of P (bf16) per wave pair
 
     // One LDS object per ring slot: Q tile, dO tile (row-major, swizzled
     // 16-byte chunks), L2 and D of the tile's rows, and the NP pairs' P
     // (at byte 2 * (2 * TILE + 4 * kBQ); see exoff below).
     // Distinct objects let the compiler tell a slot being copied from slots
     // being read (it tracks only a few copy targets).
-    constexpr int SLOT = 2 * TILE + 4 * kBQ + 2 * NP * XW;   // bf16 units
+    constexpr int SLOT = 2 * TILE + 4 * kBQ + NP * XB / 2;   // bf16 units
     __shared__ __attribute__((aligned(16))) bf16 Sl0[SLOT];
     __shared__ __attribute__((aligned(16))) bf16 Sl1[SLOT];
     __shared__ __attribute__((aligned(16))) bf16 Sl2[SLOT];
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     //  ldoff:        L2 / D values of the lane's queries, 4g floats in;
     //  exoff:        the lane's P words in the exchange area.
     int ldoff = 2 * 2 * TILE + 4 * 4 * g;
-    int exoff = 2 * (2 * TILE + 4 * kBQ) + 4 * (pair * XW + 4 * lane);
+    int exoff = 2 * (2 * TILE + 4 * kBQ) + pair * XB + 16 * lane;
     auto launder_offsets = [&]() {
         asm volatile("" : "+v"(ldoff));
         asm volatile("" : "+v"(exoff));
@@ -334,21 +336,19 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
             x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
         }
     };
-    // P exchange: word i (4 floats) of lane l of pair p at p*XW + 256i + 4l,
-    // so each 16-byte access of a wave covers 1 KB contiguously.
-    auto write_p = [&](bf16* Sd, const float* p) {
-        float* ex = (float*)at(Sd, exoff);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *(float4*)(ex + 256 * i) = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+    // P exchange (bf16, the A operands wave A already holds): 16-byte word i
+    // of lane l of pair p at byte p*XB + 1024i + 16l, so each 16-byte access
+    // of a wave covers 1 KB contiguously.
+    auto write_p = [&](bf16* Sd, const bf16x8* pa) {
+        char* ex = (char*)Sd + exoff;
+        *(bf16x8*)ex = pa[0];
+        *(bf16x8*)(ex + 1024) = pa[1];
     };
     auto read_p = [&](bf16* Sd, float* p) {
-        const float* ex = (const float*)at(Sd, exoff);
+        const char* ex = (const char*)Sd + exoff;
+        const bf16x8 a = *(const bf16x8*)ex, b = *(const bf16x8*)(ex + 1024);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 f = *(const float4*)(ex + 256 * i);
-            p[4 * i] = f.x; p[4 * i + 1] = f.y; p[4 * i + 2] = f.z; p[4 * i + 3] = f.w;
-        }
+        for (int e = 0; e < 8; ++e) { p[e] = bf2f(a[e]); p[8 + e] = bf2f(b[e]); }
     };
 
     // One step's MFMAs of a wave as a single operand stream: KK products
@@ -420,8 +420,8 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
 
     // Wave A's P of tile t (q0 = t * kBQ): zero where the key is past n_k or
     // (causal) after the query (element v's query offset 8*(v/4) + v%4 from
-    // q0 + 4g is masked iff below lim), hand the fp32 values to wave B
-    // through slot Sd and keep them as bf16 A operands for dV.
+    // q0 + 4g is masked iff below lim), round them to bf16 (A operands of
+    // dV) and hand those to wave B through slot Sd.
     auto finish_p = [&](int q0, float* p, bf16* Sd, bf16x8* pa) {
         if ((kw0 + 32 > n_k) || (CAUSAL && kw0 + 31 > q0 + coff)) {
             const int lim = key >= n_k ? 64 : (CAUSAL ? key - coff - q0 - 4 * g : -1);
@@ -429,9 +429,9 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
             for (int v = 0; v < 16; ++v)
                 if (8 * (v >> 2) + (v & 3) < lim) p[v] = 0.0f;
         }
-        write_p(Sd, p);
 #pragma unroll
         for (int v = 0; v < 16; ++v) pa[v >> 3][v & 7] = to_bf16(p[v]);
+        write_p(Sd, pa);
     };
 
     if (t_begin < nqt) {
