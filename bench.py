@@ -38,6 +38,10 @@ PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # 256 CUs x 4096 FLOP/clk x 2.4 G
 METRIC = "attention TFLOP/s fwd+bwd (bf16, causal, n=4096, d=128); % MFMA peak"
 CSRC = os.path.join(ROOT, "exact_tiled_attention_29_amd", "csrc")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_self_b2h32_n4096_d128_causal.txt")
+SQ_SUMMARY = os.path.join(ROOT, "profiles", "sq_counters_self_b2h32_n4096_d128_causal.txt")
+# Substrings of the bench kernels' mangled names in the rocprofv3 summaries.
+KERNEL_KEYS = {"fwd": "fwd_bf16", "bwd_pre": "bwd_pre_kernel", "bwd_dkdv": "bwd_dkdv",
+               "bwd_dq": "bwd_dq_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -148,6 +152,24 @@ def traffic_from_summary(kernel_key):
         if l.startswith("kernel") and kernel_key in l:
             parts = l.split()
             return float(parts[parts.index("fetch_bytes") + 1]) + float(parts[parts.index("write_bytes") + 1])
+    return None
+
+
+def counter_from_summary(kernel_key, counter):
+    """Average per dispatch of `counter` for the kernel from the SQ counter
+    summary, or None when it is missing or the kernels changed since."""
+    if not os.path.exists(SQ_SUMMARY):
+        return None
+    lines = open(SQ_SUMMARY).read().splitlines()
+    src = next((l.split()[1] for l in lines if l.startswith("source_hash")), None)
+    if src != kernel_source_hash():
+        return None
+    inside = False
+    for l in lines:
+        if l.startswith("kernel"):
+            inside = kernel_key in l
+        elif inside and l.split() and l.split()[0] == counter:
+            return float(l.split()[1])
     return None
 
 
@@ -381,13 +403,26 @@ def main():
         ach = dom_flop / (kernels[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_summary({"fwd": "fwd_bf16", "bwd_dkdv": "bwd_dkdv",
-                                                 "bwd_dq": "bwd_dq_kernel"}[dom]),
+                "traffic": traffic_from_summary(KERNEL_KEYS[dom]),
                 "kernel": dom, "avg_ms": round(kernels[dom], 4)}
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": 8000.0, "unit": "GB/s", "frac": None,
                 "traffic": None, "kernel": dom, "avg_ms": round(kernels[dom], 4)}
 
+    # Per kernel: event-timed duration, the MFMA rate of the products it runs,
+    # and (for the bench workload, when the counter summaries match the
+    # kernel sources) HBM bytes per launch over that duration and MfmaUtil.
+    flop_of = {"fwd": f_fwd, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 1.5 * f_fwd}
+    per_kernel = {}
+    for kname, t in kernels.items():
+        e = {"ms": round(t, 4)}
+        if kname in flop_of:
+            e["tflops"] = round(flop_of[kname] / (t * 1e-3) / 1e12, 1)
+        if w.name == workloads.HEADLINE:
+            tr = traffic_from_summary(KERNEL_KEYS[kname])
+            e["hbm_gb_s"] = round(tr / (t * 1e-3) / 1e9, 1) if tr is not None else None
+            e["mfma_util_pct"] = counter_from_summary(KERNEL_KEYS[kname], "MfmaUtil")
+        per_kernel[kname] = e
     log(f"[bench] {K} steps with per-kernel events: {wall_ev * 1e3 / K:.4f} ms/step")
     log(f"[bench] {K} steps: {ms_step:.4f} ms/step -> {value:.1f} TFLOP/s "
         f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.1f})")
@@ -405,6 +440,7 @@ def main():
         "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / ((t_pre + t_dkdv + t_dq) * 1e-3) / 1e12, 2),
         "kernel_ms": {k_: round(t, 4) for k_, t in kernels.items()},
+        "kernels": per_kernel,
         "ms_per_step_with_kernel_events": round(wall_ev * 1e3 / K, 4),
         "roofline": roof,
     }

@@ -65,6 +65,29 @@ def test_traffic_lookup_needs_matching_sources(tmp_path, monkeypatch):
     assert bench.traffic_from_summary("bwd_dkdv") is None
 
 
+def test_counter_lookup_needs_matching_sources(tmp_path, monkeypatch):
+    summ = tmp_path / "sq.txt"
+    summ.write_text("command: x\nsource_hash {}\nvalues: average\n"
+                    "kernel 'k_fwd_bf16_kernel'\n  MfmaUtil 48.5\n  VALUBusy 40\n"
+                    "kernel 'k_bwd_dkdv_kernel'\n  MfmaUtil 50.25\n".format(bench.kernel_source_hash()))
+    monkeypatch.setattr(bench, "SQ_SUMMARY", str(summ))
+    assert bench.counter_from_summary("fwd_bf16", "MfmaUtil") == 48.5
+    assert bench.counter_from_summary("bwd_dkdv", "MfmaUtil") == 50.25
+    assert bench.counter_from_summary("bwd_dkdv", "VALUBusy") is None
+    assert bench.counter_from_summary("bwd_dq_kernel", "MfmaUtil") is None
+    summ.write_text(summ.read_text().replace(bench.kernel_source_hash(), "0000000000000000"))
+    assert bench.counter_from_summary("fwd_bf16", "MfmaUtil") is None
+
+
+def test_summary_lookups_on_the_committed_profiles():
+    # the committed summaries name every bench kernel (when they match the sources)
+    if bench.counter_from_summary("fwd_bf16", "MfmaUtil") is None:
+        pytest.skip("committed counter summary predates the kernel sources")
+    for key in bench.KERNEL_KEYS.values():
+        assert bench.counter_from_summary(key, "MfmaUtil") is not None, key
+        assert bench.traffic_from_summary(key) is not None, key
+
+
 def test_summarize_stats_and_counters(tmp_path):
     stats = [{"Name": "bwd_dkdv_kernel", "Calls": "3", "TotalDurationNs": "3000000", "AverageNs": "1000000",
               "MinNs": "900000", "MaxNs": "1100000", "Percentage": "75.0"},
