@@ -209,8 +209,8 @@ FD_SHAPES = [(8, 8, 4), (5, 8, 3), (8, 5, 4), (1, 6, 2), (6, 1, 2), (7, 7, 1)]
 @pytest.mark.parametrize("n_q,n_k,d", FD_SHAPES)
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_finite_differences(n_q, n_k, d, causal):
-    # The spec asks the backward formula to match finite differences
-    # on n <= 8: loss <dO, O>, central differences with h = 1e-6.
+    # The backward formulas (page 3, section 1.5) against central finite
+    # differences of the loss <dO, O> on n <= 8, h = 1e-6.
     err = _fd_check(oracle.attention_head, n_q, n_k, d, causal, seed=n_q * 10 + n_k + d)
     assert err < 1e-7, err
 
