@@ -147,11 +147,13 @@ def _mask_code(causal) -> int:
     return int(causal)
 
 
-def _check(t: torch.Tensor, name: str, shape, dtype=None):
+def _check(t: torch.Tensor, name: str, shape, dtype=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU (the HIP kernels are the only implementation)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtype is not None and t.dtype != dtype:
@@ -185,19 +187,21 @@ def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None)
     n_k = k.shape[2]
     dt = _code(q.dtype)
     _check(q, "q", (B, H, n_q, d))
-    _check(k, "k", (B, H, n_k, d), q.dtype)
-    _check(v, "v", (B, H, n_k, d), q.dtype)
+    dev = q.device
+    _check(k, "k", (B, H, n_k, d), q.dtype, dev)
+    _check(v, "v", (B, H, n_k, d), q.dtype, dev)
     o_dtype = q.dtype if o_dtype is None else o_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, n_q, d), dtype=o_dtype, device=q.device)
-    _check(out, "out", (B, H, n_q, d), o_dtype)
+    _check(out, "out", (B, H, n_q, d), o_dtype, dev)
     if lse is None:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
-    _check(lse, "lse", (B, H, n_q), torch.float32)
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _code(o_dtype),
-                lse.data_ptr(), B, H, n_q, n_k, d, dt, _mask_code(causal), scale, _stream(q.device))
+    _check(lse, "lse", (B, H, n_q), torch.float32, dev)
+    with torch.cuda.device(dev):   # kernels launch on the current device
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _code(o_dtype),
+                    lse.data_ptr(), B, H, n_q, n_k, d, dt, _mask_code(causal), scale, _stream(dev))
     if st != 0:
         raise FAError(st, "fa_fwd")
     return out, lse
@@ -213,11 +217,12 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
     n_k = k.shape[2]
     dt = _code(q.dtype)
     _check(q, "q", (B, H, n_q, d))
-    _check(k, "k", (B, H, n_k, d), q.dtype)
-    _check(v, "v", (B, H, n_k, d), q.dtype)
-    _check(o, "o", (B, H, n_q, d))
-    _check(lse, "lse", (B, H, n_q), torch.float32)
-    _check(do, "do", (B, H, n_q, d), q.dtype)
+    dev = q.device
+    _check(k, "k", (B, H, n_k, d), q.dtype, dev)
+    _check(v, "v", (B, H, n_k, d), q.dtype, dev)
+    _check(o, "o", (B, H, n_q, d), None, dev)
+    _check(lse, "lse", (B, H, n_q), torch.float32, dev)
+    _check(do, "do", (B, H, n_q, d), q.dtype, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     mask = _mask_code(causal)
@@ -227,15 +232,20 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
+    _check(dq, "dq", (B, H, n_q, d), q.dtype, dev)
+    _check(dk, "dk", (B, H, n_k, d), q.dtype, dev)
+    _check(dv, "dv", (B, H, n_k, d), q.dtype, dev)
+    _check(workspace, "workspace", tuple(workspace.shape), None, dev)
     ev = None
     if events is not None:
         if len(events) != 4:
             raise ValueError("events must hold 4 torch.cuda.Event")
         ev = (ctypes.c_void_p * 4)(*[_event_handle(e) for e in events])
-    st = fa_bwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _code(o.dtype),
-                      lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      B, H, n_q, n_k, d, dt, mask, scale, workspace.data_ptr(), workspace.numel(),
-                      _stream(q.device), ev)
+    with torch.cuda.device(dev):   # kernels launch on the current device
+        st = fa_bwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _code(o.dtype),
+                          lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          B, H, n_q, n_k, d, dt, mask, scale, workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream(dev), ev)
     if st != 0:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
@@ -255,16 +265,17 @@ def row_softmax(x, scale=1.0, softmax=True, y_dtype=None, lse=None, out=None):
     rows = x.numel() // cols if cols else 0
     if lse is None:
         lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _check(lse, "lse", tuple(x.shape[:-1]), torch.float32)
+    _check(lse, "lse", tuple(x.shape[:-1]), torch.float32, x.device)
     y = None
     ydt = FA_BF16
     if softmax:
         y_dtype = x.dtype if y_dtype is None else y_dtype
         ydt = _code(y_dtype)
         y = torch.empty(x.shape, dtype=y_dtype, device=x.device) if out is None else out
-        _check(y, "out", tuple(x.shape), y_dtype)
-    st = fa_row_softmax(x.data_ptr(), dt, rows, cols, scale, lse.data_ptr(),
-                        y.data_ptr() if y is not None else None, ydt, _stream(x.device))
+        _check(y, "out", tuple(x.shape), y_dtype, x.device)
+    with torch.cuda.device(x.device):   # the kernel launches on the current device
+        st = fa_row_softmax(x.data_ptr(), dt, rows, cols, scale, lse.data_ptr(),
+                            y.data_ptr() if y is not None else None, ydt, _stream(x.device))
     if st != 0:
         raise FAError(st, "fa_row_softmax")
     return y, lse

@@ -336,3 +336,27 @@ def test_scale_argument():
     q, k, v, do = make_inputs(w, seed=5)
     res = run(q, k, v, do, False, scale=0.05)
     check_heads(res, q, k, v, do, False, "bf16", [(0, 0)], scale=0.05, tag="scale=0.05")
+
+
+def test_binding_rejects_bad_buffers():
+    # Caller-supplied gradients and workspace are checked before any launch:
+    # a wrong shape, dtype or device raises instead of writing out of bounds.
+    w = workloads.custom(1, 2, 64, 96, 64, "bf16", False)
+    q, k, v, do = make_inputs(w, seed=3)
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    o, l = fa.forward(qg, kg, vg, False)
+    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+    with pytest.raises(ValueError):
+        fa.backward(qg, kg, vg, o, l, dog, grads=(dq, dk[:, :, :50], dv))
+    with pytest.raises(TypeError):
+        fa.backward(qg, kg, vg, o, l, dog, grads=(dq.float(), dk, dv))
+    with pytest.raises(ValueError):
+        fa.backward(qg, kg, vg, o, l, dog, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(fa.FAError):
+        fa.backward(qg, kg, vg, o, l, dog, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.forward(qg, kg.cpu(), vg, False)
+    # the buffers are usable afterwards
+    fa.backward(qg, kg, vg, o, l, dog, grads=(dq, dk, dv))
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all()
