@@ -360,3 +360,24 @@ def test_binding_rejects_bad_buffers():
     fa.backward(qg, kg, vg, o, l, dog, grads=(dq, dk, dv))
     torch.cuda.synchronize()
     assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all()
+
+
+def test_side_stream():
+    # Every kernel is enqueued on the caller's current stream: running the
+    # whole path on a side stream gives bitwise the results of the default one.
+    w = workloads.custom(1, 4, 700, 700, 128, "bf16", True)
+    q, k, v, do = make_inputs(w, seed=6)
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    o, l = fa.forward(qg, kg, vg, True)
+    ref = [o.clone(), l.clone()] + [t.clone() for t in fa.backward(qg, kg, vg, o, l, dog, True)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o2, l2 = fa.forward(qg, kg, vg, True)
+        g2 = fa.backward(qg, kg, vg, o2, l2, dog, True)
+        out = [o2, l2] + list(g2)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, out):
+        assert torch.equal(a, b)
