@@ -365,6 +365,9 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         constexpr int NV1 = decltype(nv1)::value, NV2 = decltype(nv2)::value;
         constexpr int NS = KK + NJ;
         __builtin_amdgcn_sched_barrier(0);
+        // Raised issue priority for the stream (both waves): MFMAs and their
+        // operand reads go first, the other wave's VALU work fills the gaps.
+        mfma_priority(true);
         pre();
         bf16x8 op[kLook + 1];
         auto load = [&](int i) {
@@ -403,6 +406,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
             else if (i + kLook < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        mfma_priority(false);
     };
 
     const int nqt = (n_q + kBQ - 1) / kBQ;
