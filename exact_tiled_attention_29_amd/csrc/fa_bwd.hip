@@ -358,7 +358,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     // the second phase starts with its operands in registers. pre() issues
     // NPRE other LDS reads first; extra1(kk) / extra2(j) run after the MFMAs
     // of the two phases with about NV1 / NV2 VALU instructions each.
-    constexpr int kLook = 4;
+    constexpr int kLook = 3;   // with the raised priority, 3 beat 2, 4 and 5 (measured)
     auto stream = [&](const bf16* T1, f32x16& acc1, const bf16* T2, const bf16x8* X, auto&& pre,
                       auto npre, auto&& extra1, auto nv1, auto&& extra2, auto nv2) {
         constexpr int NPRE = decltype(npre)::value;

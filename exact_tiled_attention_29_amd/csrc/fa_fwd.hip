@@ -224,6 +224,10 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
                 }
             l_run += rs;
             // O^T (d x queries) += V^T P^T; V^T operands by transpose reads.
+            // Raised issue priority for these MFMAs, so they go first and the
+            // other wave's softmax fills the gaps (around the S^T MFMAs a
+            // raised priority was slower).
+            mfma_priority(true);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -234,6 +238,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
                     o[db] = mfma32(a, pb[c], o[db]);
                 }
             }
+            mfma_priority(false);
         }
     };
 
