@@ -23,7 +23,7 @@ import torch  # imported before libfa.so so the process shares torch's HIP runti
 __all__ = [
     "FA_BF16", "FA_F32", "FA_NO_MASK", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT",
     "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_row_softmax",
+    "fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_row_softmax",
     "fa_status_str", "fa_abi_version",
     "forward", "backward", "row_softmax", "FlashAttention", "attention",
 ]
@@ -37,8 +37,11 @@ FA_CAUSAL_TOP_LEFT = 1       # key j visible to query i iff j <= i
 FA_CAUSAL_BOTTOM_RIGHT = 2   # key j visible to query i iff j <= i + n_k - n_q
 
 _STATUS = {0: "FA_OK", 1: "FA_E_NULLPTR", 2: "FA_E_SHAPE", 3: "FA_E_DTYPE", 4: "FA_E_HEADDIM",
-           5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP", 8: "FA_E_CAUSAL"}
-_ABI_VERSION = 2
+           5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP", 8: "FA_E_CAUSAL", 9: "FA_E_SCRATCH"}
+_ABI_VERSION = 3
+# bytes of the library's static per-GPU scratch behind fa_bwd_noalloc
+FA_BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
+_SIZE_MAX = (1 << 64) - 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -73,6 +76,9 @@ def load_library():
     lib.fa_bwd.restype = i32
     lib.fa_bwd_timed.argtypes = lib.fa_bwd.argtypes + [vp]
     lib.fa_bwd_timed.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                   i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.fa_bwd_noalloc.restype = i32
     lib.fa_row_softmax.argtypes = [vp, i32, ctypes.c_longlong, i32, f32, vp, vp, i32, vp]
     lib.fa_row_softmax.restype = i32
     lib.fa_status_str.argtypes = [i32]
@@ -104,6 +110,12 @@ def fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n
     return load_library().fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads,
                                        n_q, n_k, d, dtype, int(causal), float(scale), workspace,
                                        workspace_bytes, stream, events)
+
+
+def fa_bwd_noalloc(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype,
+                   causal, scale, stream):
+    return load_library().fa_bwd_noalloc(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads,
+                                         n_q, n_k, d, dtype, int(causal), float(scale), stream)
 
 
 def fa_row_softmax(x, dtype, rows, cols, scale, lse, y, y_dtype, stream):
@@ -227,6 +239,8 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
         scale = 1.0 / math.sqrt(d)
     mask = _mask_code(causal)
     need = fa_bwd_workspace_bytes(B, H, n_q, n_k, d, dt, mask)
+    if need == _SIZE_MAX:    # arguments fa_bwd rejects: let it name the error
+        need = 0
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if grads is None:

@@ -4,8 +4,16 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_launch.h"
+
+// Backward scratch of fa_bwd_noalloc: one array per GPU, set up by the HIP
+// runtime when the library's code object is loaded on that GPU and held
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not the device array: the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[FA_BWD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -53,6 +61,24 @@ size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; NULL if the lookup fails.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 // Diagonal of the causal mask: key j is visible to query i iff j <= i + offset.
 int causal_offset(int causal, int n_q, int n_k) {
     return causal == FA_CAUSAL_BOTTOM_RIGHT ? n_k - n_q : 0;
@@ -62,7 +88,7 @@ int causal_offset(int causal, int n_q, int n_k) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 2; }
+int fa_abi_version(void) { return 3; }
 
 const char* fa_status_str(int status) {
     switch (status) {
@@ -75,6 +101,7 @@ const char* fa_status_str(int status) {
         case FA_E_WORKSPACE: return "workspace missing or too small";
         case FA_E_HIP: return "HIP runtime error";
         case FA_E_CAUSAL: return "causal must be 0, 1 or 2";
+        case FA_E_SCRATCH: return "problem needs more than the library's static backward scratch";
         default: return "unknown status";
     }
 }
@@ -99,16 +126,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, fl
 size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int dtype, int causal) {
     bool empty = false;
     const int o_dtype = dtype == FA_F32 ? FA_F32 : FA_BF16;
-    if (check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, 1.0f, &empty) != FA_OK) return 0;
+    if (check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, 1.0f, &empty) != FA_OK)
+        return SIZE_MAX;
     if (empty) return 0;
     return workspace_bytes((long long)batch * heads, n_q, d, dtype);
 }
 
-int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int o_dtype,
-                 const float* lse, const void* d_o, void* dq, void* dk, void* dv,
-                 int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
-                 void* workspace, size_t workspace_bytes_given, void* stream,
-                 void* const* events) {
+}  // extern "C"
+
+namespace {
+
+// The backward's host checks and launch, shared by fa_bwd_timed and
+// fa_bwd_noalloc. get_ws(need, &ws) supplies the workspace once every
+// argument has been checked (returns a status); it is not called for an
+// empty call.
+template <typename GetWs>
+int bwd_checked(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+                void* stream, void* const* events, GetWs&& get_ws) {
     bool empty = false;
     int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, scale, &empty);
     if (st != FA_OK) return st;
@@ -124,9 +160,9 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int
         return hip_status(e);
     }
     if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return FA_E_NULLPTR;
-    const size_t need = workspace_bytes(bh, n_q, d, dtype);
-    if (!workspace || workspace_bytes_given < need) return FA_E_WORKSPACE;
-    if (((uintptr_t)workspace) % kAlign != 0) return FA_E_WORKSPACE;
+    void* workspace = nullptr;
+    st = get_ws(workspace_bytes(bh, n_q, d, dtype), &workspace);
+    if (st != FA_OK) return st;
     fa::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.d_o = d_o;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -142,12 +178,45 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int
     return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
 
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                 const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                 int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+                 void* workspace, size_t workspace_bytes_given, void* stream,
+                 void* const* events) {
+    return bwd_checked(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype,
+                       causal, scale, stream, events, [&](size_t need, void** ws) {
+        if (!workspace || workspace_bytes_given < need) return (int)FA_E_WORKSPACE;
+        if (((uintptr_t)workspace) % kAlign != 0) return (int)FA_E_WORKSPACE;
+        *ws = workspace;
+        return (int)FA_OK;
+    });
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
            const float* lse, const void* d_o, void* dq, void* dk, void* dv,
            int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
            void* workspace, size_t workspace_bytes_given, void* stream) {
     return fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d,
                         dtype, causal, scale, workspace, workspace_bytes_given, stream, nullptr);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                   const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                   int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+                   void* stream) {
+    // The row-term kernel overwrites every word of the scratch that the dK/dV
+    // and dQ kernels read (padding rows included), so nothing is cleared
+    // between calls.
+    return bwd_checked(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype,
+                       causal, scale, stream, nullptr, [](size_t need, void** ws) {
+        if (need > FA_BWD_NOALLOC_SCRATCH_BYTES) return (int)FA_E_SCRATCH;
+        *ws = scratch_on_current_device();
+        return *ws ? (int)FA_OK : (int)FA_E_HIP;
+    });
 }
 
 int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float scale, float* lse,

@@ -4,8 +4,9 @@
  * C ABI of libfa.so. Every tensor argument is a HIP device pointer to a
  * contiguous row-major array; sizes are plain ints; the stream is a
  * hipStream_t passed as void* (NULL = the default stream). No call allocates
- * or frees device memory and the library keeps no global state, so calls on
- * different streams may run concurrently.
+ * or frees device memory. Apart from the static scratch of fa_bwd_noalloc
+ * the library keeps no global state, so the other calls may run
+ * concurrently on different streams.
  *
  * Layout: Q, O, dO, dQ are [batch, heads, n_q, d]; K, V, dK, dV are
  * [batch, heads, n_k, d]; L is [batch, heads, n_q]. Offsets are 64-bit.
@@ -45,7 +46,9 @@ typedef enum {
     FA_E_SCALE = 5,     /* scale not finite or not > 0                         */
     FA_E_WORKSPACE = 6, /* backward workspace NULL or smaller than required    */
     FA_E_HIP = 7,       /* a HIP launch or runtime call failed                 */
-    FA_E_CAUSAL = 8     /* causal is not one of the fa_mask values             */
+    FA_E_CAUSAL = 8,    /* causal is not one of the fa_mask values             */
+    FA_E_SCRATCH = 9    /* fa_bwd_noalloc: the problem needs more scratch than
+                           FA_BWD_NOALLOC_SCRATCH_BYTES                        */
 } fa_status;
 
 /* The `causal` argument of fa_fwd / fa_bwd. */
@@ -94,8 +97,8 @@ int fa_fwd(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (0 for an empty
  * call). bf16: the fp32 row term D and L * log2(e), each [B,H,ceil(n_q/32)*32]
- * and 256-byte aligned; float32: D [B,H,n_q]. Returns 0 for arguments
- * fa_bwd would reject.
+ * and 256-byte aligned; float32: D [B,H,n_q]. Returns SIZE_MAX for
+ * arguments fa_bwd would reject (so 0 always means an empty call).
  */
 size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
                               int dtype, int causal);
@@ -144,6 +147,30 @@ int fa_bwd_timed(const void* q, const void* k, const void* v,
                  void* workspace, size_t workspace_bytes, void* stream,
                  void* const* events);
 
+/* Size of the static per-GPU scratch behind fa_bwd_noalloc (16 MiB). */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results as fa_bwd, without the workspace. Its scratch
+ * is a static array of FA_BWD_NOALLOC_SCRATCH_BYTES in the library's code
+ * object, one per GPU, held from the first call on that GPU until the
+ * process ends; the call itself allocates nothing. It serves problems with
+ * fa_bwd_workspace_bytes(...) <= FA_BWD_NOALLOC_SCRATCH_BYTES (bf16: about
+ * 2 million query rows over all batches and heads) and returns FA_E_SCRATCH
+ * beyond that, with nothing launched. Calls on one GPU share that GPU's
+ * scratch: calls that overlap in time on the same GPU (other streams,
+ * other host threads) race and give undefined results. The first call on a
+ * GPU looks the scratch address up (hipGetSymbolAddress); a failure there
+ * returns FA_E_HIP.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v,
+                   const void* o, int o_dtype, const float* lse, const void* d_o,
+                   void* dq, void* dk, void* dv,
+                   int batch, int heads, int n_q, int n_k, int d, int dtype,
+                   int causal, float scale, void* stream);
+
 /*
  * Row softmax and logsumexp of a plain matrix: for every row r of scale * X,
  * lse[r] = ln sum_c exp(scale * X[r,c]) and, when y is not NULL,
@@ -170,7 +197,10 @@ int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float sca
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 
-/* ABI version of this header: 2 (2 added FA_CAUSAL_BOTTOM_RIGHT and FA_E_CAUSAL). */
+/* ABI version of this header: 3 (2 added FA_CAUSAL_BOTTOM_RIGHT and
+   FA_E_CAUSAL; 3 added fa_bwd_noalloc and FA_E_SCRATCH, and
+   fa_bwd_workspace_bytes returns SIZE_MAX instead of 0 for rejected
+   arguments). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

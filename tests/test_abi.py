@@ -17,8 +17,9 @@ import exact_tiled_attention_29_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULLPTR, SHAPE, DTYPE, HEADDIM, SCALE, WORKSPACE, HIP, CAUSAL = 0, 1, 2, 3, 4, 5, 6, 7, 8
+OK, NULLPTR, SHAPE, DTYPE, HEADDIM, SCALE, WORKSPACE, HIP, CAUSAL, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
 BF16, F32 = 0, 1
+REJECTED = (1 << 64) - 1   # fa_bwd_workspace_bytes for arguments fa_bwd rejects (SIZE_MAX)
 P = 0x1000  # a non-null dummy pointer; never dereferenced on the validation paths
 
 
@@ -37,8 +38,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_row_softmax",
-         "fa_status_str", "fa_abi_version"])
+        ["fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc", "fa_bwd_workspace_bytes",
+         "fa_row_softmax", "fa_status_str", "fa_abi_version"])
 
 
 def test_library_exports_every_header_function(lib):
@@ -51,8 +52,8 @@ def test_library_exports_every_header_function(lib):
 
 
 def test_status_strings(lib):
-    assert lib.fa_abi_version() == 2
-    for code in range(9):
+    assert lib.fa_abi_version() == 3
+    for code in range(10):
         s = fa.fa_status_str(code)
         assert s and s != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
@@ -118,6 +119,36 @@ def test_backward_specific_codes(lib):
     assert bwd(workspace=P + 4) == WORKSPACE  # not 256-byte aligned
 
 
+def noalloc(**kw):
+    args = dict(q=P, k=P, v=P, o=P, o_dtype=BF16, lse=P, d_o=P, dq=P, dk=P, dv=P, batch=1, heads=1,
+                n_q=8, n_k=8, d=64, dtype=BF16, causal=0, scale=0.125, stream=None)
+    args.update(kw)
+    return fa.fa_bwd_noalloc(**args)
+
+
+def test_noalloc_validation_codes(lib):
+    # the same host checks as fa_bwd, all before any HIP call
+    assert noalloc(dtype=7) == DTYPE
+    assert noalloc(n_k=0) == SHAPE
+    assert noalloc(d=80) == HEADDIM
+    assert noalloc(scale=0.0) == SCALE
+    assert noalloc(causal=3) == CAUSAL
+    assert noalloc(q=None) == NULLPTR
+    assert noalloc(d_o=None) == NULLPTR
+    assert noalloc(dq=None) == NULLPTR
+    assert noalloc(dtype=F32, o_dtype=F32, d=32, dv=None) == NULLPTR
+    # beyond the static scratch: refused with nothing launched
+    cap = fa.FA_BWD_NOALLOC_SCRATCH_BYTES
+    rows = 1 << 21                       # bf16 needs 8 bytes per padded query row
+    assert fa.fa_bwd_workspace_bytes(1, 64, rows // 64, 8, 64, BF16, 0) == cap
+    assert fa.fa_bwd_workspace_bytes(1, 64, rows // 64 + 32, 8, 64, BF16, 0) > cap
+    assert noalloc(heads=64, n_q=rows // 64 + 32) == SCRATCH
+    assert noalloc(heads=64, n_q=rows // 64 + 32, q=None) == NULLPTR   # pointers checked first
+    assert noalloc(batch=2, heads=64, n_q=rows // 64 + 1, dtype=F32, o_dtype=F32, d=32) == SCRATCH
+    # empty: nothing to compute, no scratch needed
+    assert noalloc(batch=0, q=None, dq=None) == OK
+
+
 def test_empty_forward_is_a_noop(lib):
     # Nothing to compute: returns before any HIP call, pointers untouched.
     assert fwd(n_q=0, q=None, o=None, lse=None) == OK
@@ -134,11 +165,13 @@ def test_workspace_bytes(lib):
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 1) == 2 * up(B * H * pad * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 32, F32, 0) == up(rows * 4)
     assert fa.fa_bwd_workspace_bytes(B, H, 0, n_k, d, BF16, 0) == 0
-    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 80, BF16, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 80, BF16, 0) == REJECTED
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, 96, BF16, 0) == 2 * up(B * H * pad * 4)
-    assert fa.fa_bwd_workspace_bytes(B, H, n_q, 0, d, BF16, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, 0, d, BF16, 0) == REJECTED
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 2) == 2 * up(B * H * pad * 4)
-    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 3) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, BF16, 3) == REJECTED
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, 5, 0) == REJECTED
+    assert fa.fa_bwd_workspace_bytes(B, H, -1, n_k, d, BF16, 0) == REJECTED
 
 
 def test_mask_codes_of_the_binding():
