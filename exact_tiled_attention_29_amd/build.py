@@ -7,6 +7,7 @@ objects are linked into exact_tiled_attention_29_amd/libfa.so.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -50,18 +51,49 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Kernels whose registers must never spill to scratch (a spill in the hot
+# loop puts memory waits between the MFMAs). The float32 kernels keep a
+# whole row per thread and are allowed to spill at large head dims.
+NO_SPILL = ("fwd_bf16_kernel", "fwd_pp_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+            "bwd_pre_kernel", "row_softmax_kernel")
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs Spill|ScratchSize \[bytes/lane\]|VGPRs|AGPRs|"
+                     r"Occupancy \[waves/SIMD\]):\s+(\S+)")
+
+
+def resource_usage(stderr: str):
+    """Per kernel {VGPRs, AGPRs, VGPRs Spill, ScratchSize, Occupancy} from
+    the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(stderr):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val)
+    return out
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
-           "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra,
+           "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
-    if r.stderr.strip():
-        # hipcc's host pass warns about the gfx-only feature flag; keep the rest.
-        lines = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
-        if lines:
-            sys.stderr.write("\n".join(lines) + "\n")
+    usage = resource_usage(r.stderr)
+    with open(obj + ".resources.txt", "w") as fh:
+        for name, u in sorted(usage.items()):
+            fh.write(f"{name} {u}\n")
+    spilled = [n for n, u in usage.items()
+               if any(k in n for k in NO_SPILL) and (u.get("VGPRs Spill", 0) or u.get("ScratchSize", 0))]
+    if spilled:
+        raise RuntimeError(f"{src}: kernels spill registers to scratch: {spilled}")
+    # hipcc's host pass warns about the gfx-only feature flag; keep real warnings.
+    lines = [ln for ln in r.stderr.splitlines()
+             if ln.strip() and "packed-fp32-ops" not in ln and "kernel-resource-usage" not in ln
+             and not ln.lstrip().startswith(("|", "^")) and not re.match(r"^\s*\d+ \|", ln)]
+    if lines:
+        sys.stderr.write("\n".join(lines) + "\n")
     return obj
 
 

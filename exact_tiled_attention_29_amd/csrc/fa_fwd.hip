@@ -302,9 +302,10 @@ hipError_t dispatch_mask(const FwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int fwd_bf16_rows_per_wg(const FwdArgs&) { return 128; }
+int fwd_bf16_rows_per_wg(const FwdArgs& a) { return fwd_pp_supports(a) ? 256 : 128; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
+    if (fwd_pp_supports(a)) return launch_fwd_pp(a, st);
     switch (a.d) {
         case 32: return dispatch_mask<32>(a, st);
         case 64: return dispatch_mask<64>(a, st);

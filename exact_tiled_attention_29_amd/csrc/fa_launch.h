@@ -55,6 +55,9 @@ inline int dq_rows_padded(int n_q) { return (n_q + 31) / 32 * 32; }
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
 int fwd_bf16_rows_per_wg(const FwdArgs& a);
+// Phase-locked two-group forward (fa_fwd_pp.hip) for the head dims it serves.
+bool fwd_pp_supports(const FwdArgs& a);
+hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t st);
 
 // float32 path (fp32 FMA).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);

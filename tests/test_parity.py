@@ -194,6 +194,33 @@ def test_edge_shapes(B, H, n_q, n_k, d, dtype, causal):
     check_heads(res, q, k, v, do, causal, dtype, heads, tag=str((B, H, n_q, n_k, d, dtype, causal)))
 
 
+# Shapes with 1024 (batch, head) pairs, so every forward launch has at least
+# four 256-row workgroups per CU and takes the phase-locked two-group kernel
+# (head dims 64 and 128): ragged tails, n_q != n_k both ways, every mask.
+EDGE_MANY_HEADS = [
+    (4, 256, 100, 100, 128, "bf16", True),
+    (4, 256, 333, 200, 128, "bf16", True),
+    (4, 256, 200, 333, 64, "bf16", False),
+    (4, 256, 97, 130, 128, "bf16", "bottom_right"),
+    (4, 256, 300, 81, 64, "bf16", "bottom_right"),
+    (4, 256, 257, 513, 128, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", EDGE_MANY_HEADS)
+def test_edge_shapes_many_heads(B, H, n_q, n_k, d, dtype, causal):
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
+    q, k, v, do = make_inputs(w, seed=n_q * 5 + n_k)
+    res = run(q, k, v, do, causal)
+    heads = [(0, 0), (1, 77), (3, 255)]
+    tag = str((B, H, n_q, n_k, d, dtype, causal))
+    check_heads(res, q, k, v, do, causal, dtype, heads, tag=tag)
+    # every other head through the properties that hold for any head (rows
+    # that see no key are excluded: their O and gradients are zero)
+    if causal != "bottom_right" or n_q <= n_k:
+        check_sum_invariants(res, do, dtype, tag)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_page1_backward_demo_shape(causal):
     # Page 1, section 3 demo: n = 70, d = 16, float32 here, loss sum(O^2) so dO = 2 O.
@@ -292,11 +319,14 @@ def test_empty_calls():
     assert (dk == 0).all() and (dv == 0).all()
 
 
-@pytest.mark.parametrize("d,causal,n", [(128, True, 2048), (64, False, 1024), (128, False, 1536)])
-def test_forward_is_deterministic(d, causal, n):
+@pytest.mark.parametrize("d,causal,n,bh", [(128, True, 2048, 16), (64, False, 1024, 16),
+                                           (128, False, 1536, 16), (128, True, 2048, 256),
+                                           (64, False, 1024, 256)])
+def test_forward_is_deterministic(d, causal, n, bh):
     # Repeated runs are bitwise equal (tiles are staged and consumed under
     # barriers; a tile read before every wave's copy lands shows up here).
-    w = workloads.custom(2, 8, n, n, d, "bf16", causal)
+    # 256 heads take the 256-row two-group kernel, 16 heads the 128-row one.
+    w = workloads.custom(2, bh // 2, n, n, d, "bf16", causal)
     q, k, v, _ = make_inputs(w, seed=1)
     qg, kg, vg = (t.cuda() for t in (q, k, v))
     o1, l1 = fa.forward(qg, kg, vg, causal)
