@@ -11,10 +11,11 @@
 // dQ are 0 and it adds nothing to dK, dV.
 //
 // Three kernels on one stream:
-//  1. bwd_pre:  D = rowsum(dO * O) and L2 = L * log2(e) into per-head arrays
-//     padded to a multiple of 32 rows (padding and rows with L = -inf:
+//  1. bwd_pre:  -D = -rowsum(dO * O) and L2 = L * log2(e) into per-head
+//     arrays padded to a multiple of 32 rows (padding and rows with L = -inf:
 //     L2 = +inf, D = 0, so those query rows get P = 0 and dS = 0 without any
-//     masking);
+//     masking); -D is where the dP accumulators of both later kernels start,
+//     so their MFMAs deliver dP - D;
 //  2. bwd_dkdv: key-stationary. One workgroup per 128 keys of one (batch,
 //     head); each of its 4 waves keeps 32 keys' K and V rows in registers as
 //     MFMA operands and their dK, dV in fp32 accumulators, and walks the
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
     if (prow < rows_pad && sub == 0) {
         const float lse = valid ? Lse[(size_t)bh * n_q + q] : kNegInf;
         const bool live = lse > kNegInf;
-        dp[prow] = live ? acc : 0.0f;
+        dp[prow] = live ? -acc : 0.0f;   // stored negated: the dP accumulators start from it
         l2p[prow] = live ? lse * kLog2e : __builtin_huge_valf();
     }
 }
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         const int q0 = t * kBQ;
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-            const int b = NW * i + wave;
+            const int b = 4 * i + wave;
             if (!kEvenCopies && b >= 2 * NCH) break;
             const bool is_q = b < NCH;
             const int chunk = is_q ? b : b - NCH;
@@ -269,10 +270,10 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     // extra(kk) runs after the MFMA of k-step kk and issues about NV VALU
     // instructions.
     constexpr int kLookS = 3;
-    auto rows_times_keys = [&](const bf16* Tb, f32x16& acc_s, auto&& extra, auto nv) {
+    auto rows_times_keys = [&](const bf16* Tb, f32x16& acc_s, auto&& extra, auto nv, const f32x16& init) {
         constexpr int NV = decltype(nv)::value;
         __builtin_amdgcn_sched_barrier(0);
-        acc_s = zero_f32x16();
+        acc_s = init;
         bf16x8 a[kLookS + 1];
 #pragma unroll
         for (int kk = 0; kk < kLookS && kk < KK; ++kk) a[kk] = *(const bf16x8*)at(Tb, soff[kk]);
@@ -359,8 +360,9 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     // NPRE other LDS reads first; extra1(kk) / extra2(j) run after the MFMAs
     // of the two phases with about NV1 / NV2 VALU instructions each.
     constexpr int kLook = 3;   // with the raised priority, 3 beat 2, 4 and 5 (measured)
-    auto stream = [&](const bf16* T1, f32x16& acc1, const bf16* T2, const bf16x8* X, auto&& pre,
-                      auto npre, auto&& extra1, auto nv1, auto&& extra2, auto nv2) {
+    auto stream = [&](const bf16* T1, f32x16& acc1, const f32x16& init1, const bf16* T2,
+                      const bf16x8* X, auto&& pre, auto npre, auto&& extra1, auto nv1, auto&& extra2,
+                      auto nv2) {
         constexpr int NPRE = decltype(npre)::value;
         constexpr int NV1 = decltype(nv1)::value, NV2 = decltype(nv2)::value;
         constexpr int NS = KK + NJ;
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                                              lds_read_tr(at(T2, troff[db][1] + cb)));
             }
         };
-        acc1 = zero_f32x16();
+        acc1 = init1;
 #pragma unroll
         for (int i = 0; i < kLook; ++i) load(i);
 #pragma unroll
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                 float lq[16], p[16];
                 read_rows(Sl0, 0, lq);
                 f32x16 s;
-                rows_times_keys(q_of(Sl0), s, noop, nv0);
+                rows_times_keys(q_of(Sl0), s, noop, nv0, zero_f32x16());
 #pragma unroll
                 for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(s[v], scale2, -lq[v]));
                 finish_p(t_begin * kBQ, p, Sl0, pa_p);
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                 launder_offsets();
                 float lq[16], p[16];
                 f32x16 s;
-                stream(q_of(Sc), s, do_of(Sp), pa_p, [&]() { read_rows(Sc, 0, lq); }, n_row_reads,
+                stream(q_of(Sc), s, zero_f32x16(), do_of(Sp), pa_p, [&]() { read_rows(Sc, 0, lq); }, n_row_reads,
                        noop, nv0, [&](int j) {
 #pragma unroll
                     for (int e = 0; e < EPM; ++e) {
@@ -489,23 +491,33 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
             launder_offsets();
             keys_times_tile(do_of(Sl), pa_p, noop, nv0);
         } else {
-            // dP of the previous tile (its dS is formed one step later).
+            // dP - D of the previous tile (its dS is formed one step later):
+            // the accumulators start from -D of the tile's queries (element
+            // v's query is the one of element v of read_rows).
+            auto neg_d_of = [&](bf16* Sd) {
+                float nd[16];
+                read_rows(Sd, 1, nd);
+                f32x16 x;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = nd[v];
+                return x;
+            };
             f32x16 dp_c;
-            rows_times_keys(do_of(Sl0), dp_c, noop, nv0);
-            // Step for tile t: dS of tile t-1 (from wave A's P, dP and D of
-            // t-1), dP of tile t, then dK of tile t-1. The dS work runs while
-            // wave A of the same SIMD keeps the matrix core busy.
+            rows_times_keys(do_of(Sl0), dp_c, noop, nv0, neg_d_of(Sl0));
+            // Step for tile t: dS = P * (dP - D) of tile t-1 (from wave A's
+            // P), dP - D of tile t, then dK of tile t-1. The dS work runs
+            // while wave A of the same SIMD keeps the matrix core busy.
             auto step = [&](bf16* Sc, bf16* Sp, bf16* Sf, int t) {
                 copies_barrier();  // tile t landed; P of tile t-1 written
                 if (t + 1 < nqt) issue_tile(Sf, t + 1);
                 launder_offsets();
-                float dq[16], p[16];
-                read_rows(Sp, 1, dq);
+                float p[16];
+                const f32x16 nd = neg_d_of(Sc);
                 read_p(Sp, p);
                 bf16x8 dsa[2];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * (dp_c[v] - dq[v]));
-                stream(do_of(Sc), dp_c, q_of(Sp), dsa, none, nv0, noop, nv0, noop, nv0);
+                for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * dp_c[v]);
+                stream(do_of(Sc), dp_c, nd, q_of(Sp), dsa, none, nv0, noop, nv0, noop, nv0);
             };
             for (int t = t_begin + 1; t < nqt; t += 3) {
                 step(Sl1, Sl0, Sl2, t);
@@ -515,12 +527,11 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
             copies_barrier();  // P of the last tile written
             bf16* Sl = s_last == 0 ? Sl0 : (s_last == 1 ? Sl1 : Sl2);
             launder_offsets();
-            float dq[16], p[16];
-            read_rows(Sl, 1, dq);
+            float p[16];
             read_p(Sl, p);
             bf16x8 dsa[2];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * (dp_c[v] - dq[v]));
+            for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * dp_c[v]);
             keys_times_tile(q_of(Sl), dsa, noop, nv0);
         }
     }
@@ -589,12 +600,12 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
         }
     }
     const float l2 = row < n_q ? l2p[(size_t)bh * n_q_pad + row] : __builtin_huge_valf();
-    const float drw = row < n_q ? dp[(size_t)bh * n_q_pad + row] : 0.0f;
+    const float ndrw = row < n_q ? dp[(size_t)bh * n_q_pad + row] : 0.0f;   // -D
     // Every element of a lane's dP^T accumulator belongs to the lane's query,
     // so the accumulator starts at -D and the MFMAs deliver dP - D directly.
     f32x16 neg_d;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) neg_d[v] = -drw;
+    for (int v = 0; v < 16; ++v) neg_d[v] = ndrw;
 
     int kend = n_k;
     if (CAUSAL) kend = max(0, min(n_k, min(q0 + BR, n_q) + coff));

@@ -445,8 +445,7 @@ hipError_t dispatch_pp(const FwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Compute units of the current device (cached per device; 0 if unknown).
-static int cu_count() {
+int device_cu_count() {
     static int cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -463,10 +462,7 @@ static int cu_count() {
 // (else the 128-row kernel, two workgroups per CU, balances better).
 bool fwd_pp_supports(const FwdArgs& a) {
     if (a.d != 128 && a.d != 64) return false;
-    const long long nwg = (long long)a.bh * ((a.n_q + kPPRows - 1) / kPPRows);
-    const int cus = cu_count();
-    if (cus <= 0) return false;
-    return nwg % cus == 0 || nwg >= 4LL * cus;
+    return fills_cus((long long)a.bh * ((a.n_q + kPPRows - 1) / kPPRows));
 }
 
 hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t st) {

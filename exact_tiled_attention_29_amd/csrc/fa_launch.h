@@ -37,7 +37,7 @@ struct BwdArgs {
     int coff;    // as in FwdArgs
     bool o_f32;
     float scale;
-    float* drow;    // fp32 D = rowsum(dO * O): [bh, n_q] (fp32 path) or [bh, n_q_pad] (bf16)
+    float* drow;    // fp32 D = rowsum(dO * O): [bh, n_q] (fp32 path), or -D [bh, n_q_pad] (bf16)
     float* l2pad;   // fp32 [bh, n_q_pad] L * log2(e), +inf on padding rows (bf16 path)
     hipEvent_t const* events;  // NULL or 4 events: before D, before dK/dV, after dK/dV, end
 };
@@ -55,6 +55,15 @@ inline int dq_rows_padded(int n_q) { return (n_q + 31) / 32 * 32; }
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
 int fwd_bf16_rows_per_wg(const FwdArgs& a);
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count();
+// Whether nwg workgroups of one per CU fill the CUs in whole rounds or in
+// enough rounds that the last one matters little.
+inline bool fills_cus(long long nwg) {
+    const int cus = device_cu_count();
+    return cus > 0 && (nwg % cus == 0 || nwg >= 4LL * cus);
+}
+
 // Phase-locked two-group forward (fa_fwd_pp.hip) for the head dims it serves.
 bool fwd_pp_supports(const FwdArgs& a);
 hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t st);

@@ -96,7 +96,7 @@ int fa_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (0 for an empty
- * call). bf16: the fp32 row term D and L * log2(e), each [B,H,ceil(n_q/32)*32]
+ * call). bf16: the fp32 row term -D and L * log2(e), each [B,H,ceil(n_q/32)*32]
  * and 256-byte aligned; float32: D [B,H,n_q]. Returns SIZE_MAX for
  * arguments fa_bwd would reject (so 0 always means an empty call).
  */
