@@ -7,15 +7,26 @@ resident in HBM before timing starts. The metric is attention TFLOP/s for
 fwd+bwd with the FLOP convention 4 * n_q * n_k * d per (batch, head) for the
 forward, halved under the causal mask, and 2.5x that for the backward.
 
-Prints one JSON line (the last line of stdout) with the metric, a roofline
-entry for the dominant kernel and the fp64 CPU oracle timed on a bounded
-sample of the same workload. The K timed steps run twice: first with HIP
-events recorded between the kernels on the library's stream (each kernel's
-average duration, hence the roofline; timing events add a few microseconds
-each, so that loop is reported separately as ms_per_step_with_kernel_events),
-then bare (the metric: wall clock between two device synchronisations).
+Prints one JSON line (the last line of stdout). For the headline workload
+(2 x 32 heads, 4096 tokens, d = 128, causal):
+  * value: K bare steps, wall clock between two device synchronisations;
+    step_ms: median / min / mean of those steps from one event per step;
+  * kernels / roofline: per-kernel durations from HIP events recorded
+    between the kernels in a separate loop of K steps (each event costs a
+    few microseconds, so that loop's steps are longer than bare ones); the
+    roofline entry is the dominant kernel's credited FLOPs (the method's
+    products only) per launch over its mean duration;
+  * configs: the other workloads, forward-only and fwd+bwd, median / min of
+    30 event-timed steps after 5 warm-up steps;
+  * device: rocminfo's CU count and maximum engine clock;
+  * power: socket power and GFX clock sampled with amd-smi while the
+    headline step runs back to back for a few seconds (these kernels run at
+    the chip's power limit, below the 2.4 GHz clock the peak assumes);
+  * cpu_baseline: the fp64 oracle on whole heads of each workload, on a
+    thread pool over (head, row chunk) with one BLAS thread per worker, on
+    the host cores this job may use; with the GPU/oracle time ratios.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-configs] [--no-power]
   python bench.py --shape BxHxNQxNKxD [--mask none|top_left|bottom_right]   # any bf16 shape
   python bench.py --rows [--rows-shape RxC]   # standalone row softmax kernel (HBM roofline)
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --summary-out F   # HBM bytes per kernel
@@ -40,7 +51,7 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_29_amd", "csrc")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_self_b2h32_n4096_d128_causal.txt")
 SQ_SUMMARY = os.path.join(ROOT, "profiles", "sq_counters_self_b2h32_n4096_d128_causal.txt")
 # Substrings of the bench kernels' mangled names in the rocprofv3 summaries.
-KERNEL_KEYS = {"fwd": "fwd_bf16", "bwd_pre": "bwd_pre_kernel", "bwd_dkdv": "bwd_dkdv",
+KERNEL_KEYS = {"fwd": "fwd_pp_kernel", "bwd_pre": "bwd_pre_kernel", "bwd_dkdv": "bwd_dkdv",
                "bwd_dq": "bwd_dq_kernel"}
 
 
@@ -174,30 +185,92 @@ def counter_from_summary(kernel_key, counter):
 
 
 # --------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle on a bounded sample
+# CPU baseline: the fp64 oracle on bounded samples, on the host's cores
 # --------------------------------------------------------------------------
 
-def cpu_baseline(w, q, k, v, do, n_heads):
+ORACLE_ROW_CHUNK = 512     # query rows per oracle task
+ORACLE_SAMPLE_FLOP = 2e12  # the oracle's own FLOP per timed sample (whole heads)
+CPU_SHARE = 16             # host cores a one-GPU job may use (the box's share)
+
+
+def oracle_flop_per_head(w) -> float:
+    """The oracle's own fp64 FLOP count per (batch, head) for fwd+bwd: the
+    materialised S, P V, dO V^T, dS K, dS^T Q and P^T dO products, 12 n_q n_k d
+    with no causal skip (the oracle computes full score rows)."""
+    return 12.0 * w.n_q * w.n_k * w.d
+
+
+def cpu_oracle_times(w, q, k, v, do, heads):
+    """Wall seconds of the fp64 oracle (oracle.attention_head) for the given
+    (b, h) heads, forward only and fwd+bwd, on a thread pool over (head,
+    chunk of ORACLE_ROW_CHUNK query rows) with one BLAS thread per worker
+    (numpy releases the GIL inside its kernels). A chunk's task returns its
+    rows' O, L (and dQ) and its rows' share of dK, dV; shares of one head
+    add up to the head's gradients."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:  # pragma: no cover
-        threads = 1
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    visible = len(os.sched_getaffinity(0))
+    workers = max(1, min(visible, CPU_SHARE))
     f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
-    picks = [(i % w.batch, (i * 7) % w.heads) for i in range(n_heads)]
-    t0 = time.perf_counter()
-    for b, h in picks:
-        oracle.attention_head(f(q[b, h]), f(k[b, h]), f(v[b, h]), f(do[b, h]), w.causal)
-    dt = time.perf_counter() - t0
-    flop = w.fwd_bwd_flop() / (w.batch * w.heads) * len(picks)
-    return {
-        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"{len(picks)} of {w.batch * w.heads} heads of {w.name}, fwd+bwd in fp64 "
-                  f"({dt:.1f} s; metric FLOP convention)",
-        "seconds": dt,
+    data = {(b, h): (f(q[b, h]), f(k[b, h]), f(v[b, h]), f(do[b, h])) for b, h in heads}
+    chunks = [np.arange(r0, min(r0 + ORACLE_ROW_CHUNK, w.n_q)) for r0 in range(0, w.n_q, ORACLE_ROW_CHUNK)]
+    tasks = [(hd, c) for hd in heads for c in chunks]
+
+    def run(with_grads):
+        def one(t):
+            (b, h), rows = t
+            Q, K, V, dO = data[(b, h)]
+            return oracle.attention_head(Q, K, V, dO if with_grads else None, w.causal, rows=rows,
+                                         visit=rows)
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            res = list(ex.map(one, tasks))
+        dt = time.perf_counter() - t0
+        assert all(np.isfinite(r["O"]).all() for r in res)
+        return dt
+
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t_fwd, t_all = run(False), run(True)
+    else:  # pragma: no cover
+        t_fwd, t_all = run(False), run(True)
+    return {"fwd_s": t_fwd, "fwd_bwd_s": t_all, "workers": workers, "host_cores_visible": visible}
+
+
+def cpu_baseline_entry(w, q, k, v, do, heads, gpu_fwd_ms, gpu_step_ms):
+    """Oracle times on a sample of whole heads of workload w, next to the GPU
+    times of the full workload scaled to the same heads."""
+    t = cpu_oracle_times(w, q, k, v, do, heads)
+    nbh = w.batch * w.heads
+    frac = len(heads) / nbh
+    e = {
+        "sample": f"{len(heads)} of {nbh} heads (whole heads, every query row)",
+        "oracle_fwd_s": round(t["fwd_s"], 3), "oracle_fwd_bwd_s": round(t["fwd_bwd_s"], 3),
+        "oracle_flop_fwd_bwd": oracle_flop_per_head(w) * len(heads),
+        "cores": t["workers"], "host_cores_visible": t["host_cores_visible"],
+        "metric_tflops_fwd_bwd": round(w.fwd_bwd_flop() * frac / t["fwd_bwd_s"] / 1e12, 5),
     }
+    if gpu_step_ms:
+        e["gpu_over_oracle_fwd_bwd"] = round(t["fwd_bwd_s"] / (gpu_step_ms * 1e-3 * frac), 1)
+    if gpu_fwd_ms:
+        e["gpu_over_oracle_fwd"] = round(t["fwd_s"] / (gpu_fwd_ms * 1e-3 * frac), 1)
+    return e
+
+
+def oracle_sample(w):
+    """Whole heads the oracle times for workload w: at most 2e12 of its fp64
+    FLOP (several seconds on 16 cores: every head of the 4096-token and
+    smaller workloads) or a single head."""
+    nbh = w.batch * w.heads
+    per_head = oracle_flop_per_head(w)
+    n = max(1, min(nbh, int(ORACLE_SAMPLE_FLOP // per_head)))
+    idx = [(i * 7) % nbh for i in range(n)] if n < nbh else list(range(nbh))
+    return [(i // w.heads, i % w.heads) for i in sorted(set(idx))]
 
 
 # --------------------------------------------------------------------------
@@ -254,8 +327,162 @@ def bench_rows(args):
 
 
 # --------------------------------------------------------------------------
+# Device facts: rocminfo's CU count and clock, and power / clock under load
+# --------------------------------------------------------------------------
+
+def device_info():
+    """CU count and max engine clock of the gfx950 agent from rocminfo."""
+    import re
+    import subprocess
+    info = {"rocminfo_compute_units": None, "rocminfo_max_clock_mhz": None, "name": None}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:  # pragma: no cover
+        return info
+    for agent in out.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        m = re.search(r"Compute Unit:[ \t]+(\d+)", agent)
+        c = re.search(r"Max Clock Freq\. \(MHz\):[ \t]+(\d+)", agent)
+        n = re.search(r"Marketing Name:[ \t]*(\S.*)", agent)
+        info["rocminfo_compute_units"] = int(m.group(1)) if m else None
+        info["rocminfo_max_clock_mhz"] = int(c.group(1)) if c else None
+        info["name"] = n.group(1).strip() if n else None
+        break
+    return info
+
+
+def parse_amd_smi(text):
+    """Socket power (W) and the first GFX clock (MHz) from `amd-smi metric -p
+    -c` output; None where absent."""
+    import re
+    p = re.search(r"SOCKET_POWER:\s*([\d.]+)\s*W", text)
+    c = re.search(r"GFX_0:\s*\n\s*CLK:\s*([\d.]+)\s*MHz", text)
+    return (float(p.group(1)) if p else None, float(c.group(1)) if c else None)
+
+
+def sustained_power(step, seconds):
+    """Run step() back to back for about `seconds` while sampling amd-smi
+    twice from a side thread; returns the mean socket power and GFX clock."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    if not shutil.which("amd-smi"):
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(min(1.5, seconds / 3))
+        while not stop.is_set() and len(samples) < 2:
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True,
+                                     text=True, timeout=20).stdout
+                samples.append(parse_amd_smi(out))
+            except Exception:  # pragma: no cover
+                break
+            time.sleep(0.5)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and (th.is_alive() or time.perf_counter() - t0 < 1.0):
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    pw = [p for p, _ in samples if p is not None]
+    ck = [c for _, c in samples if c is not None]
+    if not pw and not ck:
+        return None
+    clk = sum(ck) / len(ck) if ck else None
+    return {"socket_power_w": round(sum(pw) / len(pw), 1) if pw else None,
+            "gfx_clock_mhz": round(clk, 1) if clk else None,
+            "samples": len(samples)}
+
+
+# --------------------------------------------------------------------------
 # GPU benchmark
 # --------------------------------------------------------------------------
+
+def _stats(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    med = ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+    return {"median": round(med, 5), "min": round(ys[0], 5), "mean": round(sum(ys) / n, 5)}
+
+
+def time_per_step(fn, steps, warmup):
+    """Per-step GPU times (ms) from events recorded between steps on the
+    current stream, after warmup untimed steps."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+class Problem:
+    """Device buffers of one workload and its fwd / fwd+bwd step functions."""
+
+    def __init__(self, w, cpu_inputs=None):
+        import torch
+        import exact_tiled_attention_29_amd as fa
+        import workloads
+        self.w = w
+        self.cpu = cpu_inputs if cpu_inputs is not None else workloads.make_inputs(w)
+        dev = torch.device("cuda:0")
+        self.q, self.k, self.v, self.do = (t.to(dev) for t in self.cpu)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(w.batch, w.heads, w.n_q, dtype=torch.float32, device=dev)
+        self.grads = (torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v))
+        dt = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+        need = fa.fa_bwd_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.d, dt, fa._mask_code(w.causal))
+        self.ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+        self.fa = fa
+
+    def fwd(self, ev=None):
+        if ev is not None:
+            ev[0].record()
+        self.fa.forward(self.q, self.k, self.v, self.w.causal, out=self.o, lse=self.lse)
+        if ev is not None:
+            ev[1].record()
+
+    def step(self, evf=None, evb=None):
+        self.fwd(evf)
+        self.fa.backward(self.q, self.k, self.v, self.o, self.lse, self.do, self.w.causal,
+                         workspace=self.ws, grads=self.grads, events=evb)
+
+
+def config_entry(name, steps=30, warmup=5):
+    """Forward-only and fwd+bwd times of a named workload (median and min of
+    `steps` event-timed steps) with the metric's FLOP convention."""
+    import workloads
+    w = workloads.WORKLOADS[name]
+    pr = Problem(w)
+    f = _stats(time_per_step(pr.fwd, steps, warmup))
+    a = _stats(time_per_step(pr.step, steps, warmup))
+    fl_f, fl_a = w.fwd_flop(), w.fwd_bwd_flop()
+    e = {"workload": name, "dtype": w.dtype, "causal": w.causal,
+         "shape": [w.batch, w.heads, w.n_q, w.n_k, w.d],
+         "fwd_ms": f, "fwd_bwd_ms": a,
+         "fwd_tflops": round(fl_f / (f["median"] * 1e-3) / 1e12, 2),
+         "fwd_bwd_tflops": round(fl_a / (a["median"] * 1e-3) / 1e12, 2)}
+    if w.dtype == "bf16":
+        e["fwd_pct_of_peak"] = round(100 * e["fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+        e["fwd_bwd_pct_of_peak"] = round(100 * e["fwd_bwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+    log(f"[bench] {name}: fwd {f['median']:.4f} ms ({e['fwd_tflops']} TFLOP/s), fwd+bwd "
+        f"{a['median']:.4f} ms ({e['fwd_bwd_tflops']} TFLOP/s) [median of {steps}]")
+    return e, pr
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -268,8 +495,12 @@ def main():
                          "headline metric)")
     ap.add_argument("--mask", default="top_left", choices=["none", "top_left", "bottom_right"],
                     help="mask of --shape")
-    ap.add_argument("--cpu-heads", type=int, default=10, help="heads the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' fwd and fwd+bwd times (the 'configs' entry)")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the sustained run that samples socket power and clock")
+    ap.add_argument("--power-seconds", type=float, default=4.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -318,23 +549,21 @@ def main():
                              name=f"b{B}h{H}_q{NQ}_k{NK}_d{D}_{args.mask}")
     else:
         w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
-    metric = METRIC if w.name == workloads.HEADLINE else \
+    headline = w.name == workloads.HEADLINE
+    metric = METRIC if headline else \
         f"attention TFLOP/s fwd+bwd ({w.dtype}, mask {w.causal}, n_q={w.n_q}, n_k={w.n_k}, d={w.d})"
     fa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    dinfo = device_info()
+    dinfo["torch_multi_processor_count"] = props.multi_processor_count
+    log(f"[bench] device {dinfo.get('name') or props.name}: {dinfo['rocminfo_compute_units']} CUs, "
+        f"max clock {dinfo['rocminfo_max_clock_mhz']} MHz (rocminfo)")
 
     log(f"[bench] workload {w.name}: B={w.batch} H={w.heads} n_q={w.n_q} n_k={w.n_k} d={w.d} "
         f"{w.dtype} causal={w.causal}")
-    q, k, v, do = workloads.make_inputs(w)
-    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
-    o = torch.empty_like(qg)
-    lse = torch.empty(w.batch, w.heads, w.n_q, dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
-    ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.d,
-                                                      fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32,
-                                                      fa._mask_code(w.causal))),
-                     dtype=torch.uint8, device=dev)
+    pr = Problem(w)
 
     if args.copy_mib:
         a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -343,24 +572,16 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step(evf=None, evb=None):
-        if evf is not None:
-            evf[0].record()
-        fa.forward(qg, kg, vg, w.causal, out=o, lse=lse)
-        if evf is not None:
-            evf[1].record()
-        fa.backward(qg, kg, vg, o, lse, dog, w.causal, workspace=ws, grads=(dq, dk, dv), events=evb)
-
     for _ in range(args.warmup):
-        step()
+        pr.step()
     torch.cuda.synchronize()
 
     K = args.steps
     # Timed region 1, the per-kernel durations: K steps with HIP events
-    # recorded between the kernels on the library's stream. Each timing event
-    # costs a few microseconds of GPU time, so this loop is kept out of the
-    # metric; it also brings the GPU to its sustained clock (the first tens of
-    # steps after a pause run several percent slower).
+    # recorded between the kernels on the library's stream (torch's current
+    # stream). Each timing event costs a few microseconds of GPU time, so
+    # the kernel times add up to more than a bare step; this loop is not the
+    # metric. It also brings the GPU to its sustained clock.
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     evf = [[E(), E()] for _ in range(K)]
     evb = [[E(), E(), E(), E()] for _ in range(K)]
@@ -370,64 +591,75 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(K):
-        step(evf[i], evb[i])
+        pr.step(evf[i], evb[i])
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t1
 
-    # Timed region 2, the metric: K steps with nothing else on the stream,
-    # wall clock between two device synchronisations.
+    # Timed region 2, the metric: K steps, wall clock between two device
+    # synchronisations; one event per step boundary gives the per-step
+    # median and min.
+    sev = [E() for _ in range(K + 1)]
+    for x in sev:
+        x.record()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(K):
-        step()
+    sev[0].record()
+    for i in range(K):
+        pr.step()
+        sev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = [sev[i].elapsed_time(sev[i + 1]) for i in range(K)]
 
-    ms = lambda a, b: a.elapsed_time(b)  # noqa: E731
-    t_fwd = sum(ms(*e) for e in evf) / K
-    t_pre = sum(ms(e[0], e[1]) for e in evb) / K
-    t_dkdv = sum(ms(e[1], e[2]) for e in evb) / K
-    t_dq = sum(ms(e[2], e[3]) for e in evb) / K
+    kern = {
+        "fwd": [a.elapsed_time(b) for a, b in evf],
+        "bwd_pre": [e[0].elapsed_time(e[1]) for e in evb],
+        "bwd_dkdv": [e[1].elapsed_time(e[2]) for e in evb],
+        "bwd_dq": [e[2].elapsed_time(e[3]) for e in evb],
+    }
+    kstats = {k_: _stats(v_) for k_, v_ in kern.items()}
     ms_step = wall * 1e3 / K
-
     f_fwd = w.fwd_flop()
-    f_bwd = 2.5 * f_fwd
     f_all = w.fwd_bwd_flop()
     value = f_all / (ms_step * 1e-3) / 1e12
-    kernels = {"fwd": t_fwd, "bwd_pre": t_pre, "bwd_dkdv": t_dkdv, "bwd_dq": t_dq}
-    dom = max(kernels, key=kernels.get)
-    # FLOPs each kernel's products need: forward S and PV (2 products); dK/dV
-    # kernel S, dP, dV, dK (4); dQ kernel S, dP recomputed and dQ (3). One
-    # product over all (b, h) is half the forward count.
-    dom_flop = {"fwd": f_fwd, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 1.5 * f_fwd}.get(dom)
-    if dom_flop is not None:
-        ach = dom_flop / (kernels[dom] * 1e-3) / 1e12
+    mean_ms = {k_: st["mean"] for k_, st in kstats.items()}
+    dom = max(mean_ms, key=mean_ms.get)
+    # Credited FLOPs per kernel: the method's own products, one product =
+    # half the forward count. Forward: S and PV. dK/dV kernel: the S
+    # recompute, dV, dP and dK (4). dQ kernel: dQ only; the S and dP it
+    # forms again are work the split costs, not the method's, and are not
+    # credited (they are in "executed_tflops").
+    credit = {"fwd": 1.0, "bwd_dkdv": 2.0, "bwd_dq": 0.5}
+    executed = {"fwd": 1.0, "bwd_dkdv": 2.0, "bwd_dq": 1.5}
+    if w.dtype == "bf16" and dom in credit:
+        ach = credit[dom] * f_fwd / (mean_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_summary(KERNEL_KEYS[dom]),
-                "kernel": dom, "avg_ms": round(kernels[dom], 4)}
+                "traffic": traffic_from_summary(KERNEL_KEYS[dom]) if headline else None,
+                "kernel": dom, "avg_ms": round(mean_ms[dom], 4),
+                "algorithmic_flop": credit[dom] * f_fwd}
     else:
-        roof = {"bound": "hbm", "achieved": None, "peak": 8000.0, "unit": "GB/s", "frac": None,
-                "traffic": None, "kernel": dom, "avg_ms": round(kernels[dom], 4)}
+        roof = {"bound": "mfma", "achieved": None, "peak": round(PEAK_BF16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": None, "traffic": None, "kernel": dom,
+                "avg_ms": round(mean_ms[dom], 4)}
 
-    # Per kernel: event-timed duration, the MFMA rate of the products it runs,
-    # and (for the bench workload, when the counter summaries match the
-    # kernel sources) HBM bytes per launch over that duration and MfmaUtil.
-    flop_of = {"fwd": f_fwd, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 1.5 * f_fwd}
     per_kernel = {}
-    for kname, t in kernels.items():
-        e = {"ms": round(t, 4)}
-        if kname in flop_of:
-            e["tflops"] = round(flop_of[kname] / (t * 1e-3) / 1e12, 1)
-        if w.name == workloads.HEADLINE:
+    for kname, st in kstats.items():
+        e = {"ms": st}
+        if kname in credit:
+            e["tflops"] = round(credit[kname] * f_fwd / (st["mean"] * 1e-3) / 1e12, 1)
+            e["executed_tflops"] = round(executed[kname] * f_fwd / (st["mean"] * 1e-3) / 1e12, 1)
+        if headline:
             tr = traffic_from_summary(KERNEL_KEYS[kname])
-            e["hbm_gb_s"] = round(tr / (t * 1e-3) / 1e9, 1) if tr is not None else None
+            e["hbm_gb_s"] = round(tr / (st["mean"] * 1e-3) / 1e9, 1) if tr is not None else None
             e["mfma_util_pct"] = counter_from_summary(KERNEL_KEYS[kname], "MfmaUtil")
         per_kernel[kname] = e
     log(f"[bench] {K} steps with per-kernel events: {wall_ev * 1e3 / K:.4f} ms/step")
     log(f"[bench] {K} steps: {ms_step:.4f} ms/step -> {value:.1f} TFLOP/s "
-        f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.1f})")
-    for kname, t in kernels.items():
-        log(f"[bench]   {kname:15s} {t:.4f} ms")
+        f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.1f}); per step median "
+        f"{_stats(step_ms)['median']:.4f} min {_stats(step_ms)['min']:.4f} ms")
+    for kname, st in kstats.items():
+        log(f"[bench]   {kname:15s} {st['mean']:.4f} ms (median {st['median']:.4f}, min {st['min']:.4f})")
 
     result = {
         "metric": metric, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -437,19 +669,61 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n_q": w.n_q,
                    "n_k": w.n_k, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / ((t_pre + t_dkdv + t_dq) * 1e-3) / 1e12, 2),
-        "kernel_ms": {k_: round(t, 4) for k_, t in kernels.items()},
+        "step_ms": _stats(step_ms),
+        "fwd_tflops": round(f_fwd / (kstats["fwd"]["mean"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(2.5 * f_fwd / (sum(kstats[k_]["mean"] for k_ in ("bwd_pre", "bwd_dkdv", "bwd_dq"))
+                                           * 1e-3) / 1e12, 2),
+        "kernel_ms": {k_: st["mean"] for k_, st in kstats.items()},
         "kernels": per_kernel,
         "ms_per_step_with_kernel_events": round(wall_ev * 1e3 / K, 4),
+        "device": dinfo,
         "roofline": roof,
     }
+
+    # The other workloads: fwd and fwd+bwd, median and min of 30 steps each.
+    cfg_probs = {}
+    if headline and not args.no_configs:
+        configs = {}
+        for name in ("tiny_f32", "tiny_f32_causal", "self_b4h16_n1024_d64",
+                     "long_b1h8_n32768_d128_causal", "cross_b8h12_q1000_k3000_d64"):
+            configs[name], cfg_probs[name] = config_entry(name)
+        result["configs"] = configs
+
+    # Socket power and clock while the headline step runs back to back: the
+    # chip runs these kernels at its power limit, below its 2.4 GHz peak clock.
+    if not args.no_power:
+        pw = sustained_power(pr.step, args.power_seconds)
+        if pw and pw.get("gfx_clock_mhz"):
+            cus = dinfo["rocminfo_compute_units"] or props.multi_processor_count
+            pw["mfma_peak_at_clock_tflops"] = round(cus * 4096 * pw["gfx_clock_mhz"] * 1e6 / 1e12, 1)
+            pw["pct_of_peak_at_clock"] = round(100 * value / pw["mfma_peak_at_clock_tflops"], 2)
+        result["power"] = pw
+        if pw:
+            log(f"[bench] sustained: {pw.get('socket_power_w')} W, GFX clock {pw.get('gfx_clock_mhz')} MHz")
+
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the fp64 oracle on {args.cpu_heads} heads ...")
-        cb = cpu_baseline(w, q, k, v, do, args.cpu_heads)
-        log(f"[bench] oracle: {cb['value']:.4f} TFLOP/s on {cb['cores']} threads ({cb['seconds']:.1f} s)")
-        cb.pop("seconds")
-        result["cpu_baseline"] = cb
+        log(f"[bench] timing the fp64 oracle on {len(os.sched_getaffinity(0))} visible cores "
+            f"(pool of at most {CPU_SHARE}) ...")
+        heads = oracle_sample(w)
+        cb = cpu_baseline_entry(w, *pr.cpu, heads, kstats["fwd"]["median"], _stats(step_ms)["median"])
+        result["cpu_baseline"] = {
+            "value": cb["metric_tflops_fwd_bwd"], "unit": "TFLOP/s", "cores": cb["cores"],
+            "kind": "oracle",
+            "sample": f"{cb['sample']} of {w.name}, fwd+bwd in fp64 on a pool of {cb['cores']} threads "
+                      f"({cb['oracle_fwd_bwd_s']} s; metric FLOP convention)",
+            "detail": cb,
+        }
+        log(f"[bench] oracle {w.name}: {cb['oracle_fwd_bwd_s']} s fwd+bwd, {cb['oracle_fwd_s']} s fwd "
+            f"on {len(heads)} heads; GPU is {cb.get('gpu_over_oracle_fwd_bwd')}x faster")
+        if cfg_probs:
+            per_cfg = {}
+            for name, p_ in cfg_probs.items():
+                c = result["configs"][name]
+                per_cfg[name] = cpu_baseline_entry(p_.w, *p_.cpu, oracle_sample(p_.w),
+                                                   c["fwd_ms"]["median"], c["fwd_bwd_ms"]["median"])
+                log(f"[bench] oracle {name}: {per_cfg[name]['oracle_fwd_bwd_s']} s fwd+bwd "
+                    f"({per_cfg[name]['sample']})")
+            result["cpu_baseline"]["configs"] = per_cfg
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -137,7 +137,7 @@ def _scores(Qr, K, row_ids, off, scale):
 
 
 def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=None,
-                   row_chunk=ROW_CHUNK):
+                   row_chunk=ROW_CHUNK, visit=None):
     """Exact attention for one head, in float64.
 
     Q: (n_q, d); K, V: (n_k, d); dO: (n_q, d) or None for forward only.
@@ -154,6 +154,12 @@ def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=N
     are visited and only the requested ones are kept, unless cols is empty:
     then only the requested rows are visited (their O, L and dQ need no
     other row).
+
+    visit: optionally, exactly the query rows whose score rows are formed
+    (global indices, containing rows). dK and dV are then the sums over
+    these rows only; over any partition of the rows such partial sums add up
+    to the full gradients (dK and dV are sums over query rows), which lets a
+    caller spread one head over several workers.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -164,6 +170,7 @@ def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=N
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
     cols = np.arange(n_k) if cols is None else np.asarray(cols, dtype=np.int64)
+    visit_given = visit
     want_bwd = dO is not None
     if want_bwd:
         dO = np.asarray(dO, dtype=np.float64)
@@ -179,6 +186,8 @@ def attention_head(Q, K, V, dO=None, causal=False, scale=None, rows=None, cols=N
         visit = np.arange(n_q) if len(cols) else np.unique(rows)
     else:
         visit = np.unique(rows)
+    if visit_given is not None:
+        visit = np.unique(np.asarray(visit_given, dtype=np.int64))
 
     off = causal_offset(causal, n_q, n_k)
     for c0 in range(0, len(visit), row_chunk):

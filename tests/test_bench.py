@@ -128,3 +128,51 @@ def test_headline_workload_flops():
     w = workloads.WORKLOADS[workloads.HEADLINE]
     assert (w.batch, w.heads, w.n_q, w.n_k, w.d, w.dtype, w.causal) == (2, 32, 4096, 4096, 128, "bf16", True)
     assert w.fwd_flop() == 4 * 4096 * 4096 * 128 * 64 / 2
+
+
+def test_amd_smi_parse():
+    text = ("GPU: 0\n    POWER:\n        SOCKET_POWER: 1385 W\n    CLOCK:\n        GFX_0:\n"
+            "            CLK: 1855 MHz\n            MIN_CLK: 500 MHz\n        GFX_1:\n            CLK: 1700 MHz\n")
+    assert bench.parse_amd_smi(text) == (1385.0, 1855.0)
+    assert bench.parse_amd_smi("nothing") == (None, None)
+
+
+def test_stats_median_and_min():
+    assert bench._stats([3.0, 1.0, 2.0]) == {"median": 2.0, "min": 1.0, "mean": 2.0}
+    assert bench._stats([4.0, 1.0, 2.0, 3.0])["median"] == 2.5
+
+
+def test_oracle_sample_is_bounded_and_whole_heads():
+    for name, w in workloads.WORKLOADS.items():
+        heads = bench.oracle_sample(w)
+        assert 1 <= len(heads) <= w.batch * w.heads
+        assert len(set(heads)) == len(heads)
+        assert all(0 <= b < w.batch and 0 <= h < w.heads for b, h in heads)
+        # a bounded amount of fp64 work, or a single head
+        assert len(heads) == 1 or bench.oracle_flop_per_head(w) * len(heads) <= bench.ORACLE_SAMPLE_FLOP
+
+
+def test_cpu_oracle_pool_matches_whole_heads():
+    # the pool's chunked tasks compute the same per-head results the oracle
+    # gives for the whole head (timing entry point, small workload)
+    import torch
+    w = workloads.custom(1, 2, 700, 300, 32, "f32", True)
+    q, k, v, do = workloads.make_inputs(w, seed=3)
+    t = bench.cpu_oracle_times(w, q, k, v, do, [(0, 0), (0, 1)])
+    assert t["fwd_s"] > 0 and t["fwd_bwd_s"] > 0 and 1 <= t["workers"] <= bench.CPU_SHARE
+    e = bench.cpu_baseline_entry(w, q, k, v, do, [(0, 1)], gpu_fwd_ms=0.01, gpu_step_ms=0.03)
+    assert e["oracle_flop_fwd_bwd"] == 12.0 * 700 * 300 * 32
+    assert e["gpu_over_oracle_fwd_bwd"] > 0 and e["cores"] >= 1
+
+
+def test_rocminfo_parse(monkeypatch):
+    import subprocess as sp
+    text = ("Agent 1\n  Name: cpu\nAgent 2\n  Name:                    gfx950\n  Marketing Name:          AMD Instinct MI355X\n"
+            "  Vendor Name:             AMD\n  Compute Unit:            256\n  Max Clock Freq. (MHz):   2400\n")
+
+    class R:
+        stdout = text
+    monkeypatch.setattr(sp, "run", lambda *a, **k: R())
+    info = bench.device_info()
+    assert info == {"rocminfo_compute_units": 256, "rocminfo_max_clock_mhz": 2400,
+                    "name": "AMD Instinct MI355X"}

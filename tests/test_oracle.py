@@ -269,6 +269,29 @@ def test_chunking_and_sampling_are_exact(causal):
     assert q["dK"].shape == (0, 8) and q["dV"].shape == (0, 8)
 
 
+@pytest.mark.parametrize("causal", [False, True, "bottom_right"])
+def test_partial_row_sets_add_up(causal):
+    # A partition of the query rows into visited sets: O, L, dQ of each set
+    # are the full result's rows, and the partial dK, dV sum to the full ones
+    # (both are sums over query rows). Parallel timing of the oracle relies
+    # on this.
+    Q, K, V, dO = _rand_head(75, 60, 8, seed=21)
+    full = oracle.attention_head(Q, K, V, dO, causal=causal)
+    dK = np.zeros_like(full["dK"])
+    dV = np.zeros_like(full["dV"])
+    for part in (np.arange(0, 30), np.arange(30, 31), np.arange(31, 75)):
+        r = oracle.attention_head(Q, K, V, dO, causal=causal, rows=part, visit=part, row_chunk=16)
+        for key in ("O", "L", "dQ"):
+            np.testing.assert_allclose(r[key], full[key][part], rtol=0, atol=1e-13)
+        dK += r["dK"]
+        dV += r["dV"]
+    np.testing.assert_allclose(dK, full["dK"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dV, full["dV"], rtol=0, atol=1e-12)
+    # a proper subset alone is not the full gradient
+    r = oracle.attention_head(Q, K, V, dO, causal=causal, rows=np.arange(30), visit=np.arange(30))
+    assert np.abs(r["dV"] - full["dV"]).max() > 1e-3
+
+
 def test_batched_wrappers_match_heads():
     r = rng(14)
     Q, K, V, dO = (r.normal(size=(2, 3, 20, 8)) for _ in range(4))
