@@ -200,7 +200,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         const int q0 = t * kBQ;
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-            const int b = 4 * i + wave;
+            const int b = NW * i + wave;
             if (!kEvenCopies && b >= 2 * NCH) break;
             const bool is_q = b < NCH;
             const int chunk = is_q ? b : b - NCH;

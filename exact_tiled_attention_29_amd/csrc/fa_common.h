@@ -54,6 +54,20 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// acc + the sum of the 8 bf16 values of x (as fp32), with two-element dot
+// products against (1, 1) (v_dot2c_f32_bf16): the exact sum of the rounded
+// values that an MFMA operand carries.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2_t pr = {x[2 * i], x[2 * i + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+    return acc;
+}
+
 // fp32 -> bf16, round to nearest even (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 

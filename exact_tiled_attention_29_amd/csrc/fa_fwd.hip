@@ -107,7 +107,10 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
         }
     };
 
-    float m_ref = kNegInf, l_run = 0.0f;
+    // l_run: sum of the fp32 probabilities (for L); lb_run: sum of their
+    // bf16 roundings, the weights the PV product actually applied (for O),
+    // so the rounding of a dominant weight cancels in O / lb.
+    float m_ref = kNegInf, l_run = 0.0f, lb_run = 0.0f;
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = zero_f32x16();
@@ -205,6 +208,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
                 const float m_new = fmaxf(m_ref, mx);
                 const float corr = fast_exp2(m_ref - (m_new == kNegInf ? 0.0f : m_new));
                 l_run *= corr;
+                lb_run *= corr;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -223,6 +227,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
                     pb[2 * kb + (v >> 3)][v & 7] = to_bf16(p);
                 }
             l_run += rs;
+            lb_run += sum_bf16x8(pb[0], sum_bf16x8(pb[1], 0.0f)) + sum_bf16x8(pb[2], sum_bf16x8(pb[3], 0.0f));
             // O^T (d x queries) += V^T P^T; V^T operands by transpose reads.
             // Raised issue priority for these MFMAs, so they go first and the
             // other wave's softmax fills the gaps (around the S^T MFMAs a
@@ -257,10 +262,10 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
 
     // Epilogue: O / l, L = ln 2 * (m + log2 l). A row that saw no key has
     // l = 0 and m = -inf: O = 0 and L = -inf.
-    const float l = halves_sum(l_run);
+    const float l = halves_sum(l_run), lb = halves_sum(lb_run);
     const int row = qw + r;
     if (row < n_q) {
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
         const size_t obase = ((size_t)bh * n_q + row) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)

@@ -26,8 +26,12 @@
 //    copies use issue slots the matrix stream leaves free and have two
 //    steps to land; the tile read path carries half the bytes of two
 //    independent 128-row workgroups per CU.
-//  * scores in the exp2 domain, l sums fp32 probabilities, the PV operand
-//    is P rounded to bf16 (RNE). The VALU is the scarce unit here (while
+//  * scores in the exp2 domain, the PV operand is P rounded to bf16 (RNE);
+//    l sums the fp32 probabilities (for L), and O is divided by the sum of
+//    the bf16 values the PV product applied, so the rounding of a dominant
+//    weight cancels between numerator and denominator (with the reference
+//    max up to 2^8 below the row max, that weight's rounding reaches 2^-8
+//    and would show in O at 1e-2 on peaked rows). The VALU is the scarce unit here (while
 //    the other wave streams MFMAs it issues at about half rate), so a tile
 //    first takes its exponentials against the current reference max without
 //    computing its own max; only when that lets a value exceed 2^8 (or on
@@ -153,7 +157,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
         return (const bf16*)((const char*)base + byte_off);
     };
 
-    float m_ref = kNegInf, l_run = 0.0f;
+    // l_run: sum of the fp32 probabilities (for L); lb_run: sum of their
+    // bf16 roundings, the weights the PV product actually applied (for O).
+    float m_ref = kNegInf, l_run = 0.0f, lb_run = 0.0f;
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = zero_f32x16();
@@ -275,6 +281,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
             const float m_new = fmaxf(m_ref, mx);
             const float corr = fast_exp2(m_ref - (m_new == kNegInf ? 0.0f : m_new));
             l_run *= corr;
+            lb_run *= corr;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -311,6 +318,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
             rs = exp_tile(m_ref == kNegInf ? 0.0f : m_ref);
         }
         l_run += rs;
+        // (two chains for the bf16 sum of the P operands)
+        lb_run += sum_bf16x8(pb[0], sum_bf16x8(pb[1], 0.0f)) + sum_bf16x8(pb[2], sum_bf16x8(pb[3], 0.0f));
     };
 
     auto mid_barrier = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
@@ -401,10 +410,10 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
 
     // Epilogue: O / l, L = ln 2 * (m + log2 l); a row that saw no key gets
     // O = 0, L = -inf.
-    const float l = halves_sum(l_run);
+    const float l = halves_sum(l_run), lb = halves_sum(lb_run);
     const int row = qw + r;
     if (row < n_q) {
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
         const size_t obase = ((size_t)bh * n_q + row) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)

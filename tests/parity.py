@@ -15,6 +15,8 @@ exactly as the oracle defines it: O = 0, L = -inf, dQ = 0.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -51,17 +53,93 @@ def run(q, k, v, do, causal, scale=None, backward=True):
     return res
 
 
+def oracle_heads(Q, K, V, dO, causal, heads, scale=None, rows=None, cols=None):
+    """oracle.attention_head for several (b, h) heads at once, on a thread
+    pool (numpy releases the GIL in its kernels; one BLAS thread per worker)
+    over the heads and, when every key row is wanted, over chunks of query
+    rows whose partial dK, dV are summed. Returns {(b, h): result}."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    n_q = Q.shape[2]
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16))
+    chunk = 512
+    split = dO is not None and (cols is None or len(cols)) and rows is None
+    tasks = []
+    for hd in heads:
+        if split:
+            for r0 in range(0, n_q, chunk):
+                tasks.append((hd, np.arange(r0, min(n_q, r0 + chunk))))
+        else:
+            tasks.append((hd, None))
+
+    def one(t):
+        (b, h), part = t
+        if part is None:
+            return oracle.attention_head(Q[b, h], K[b, h], V[b, h], None if dO is None else dO[b, h],
+                                         causal, scale, rows=rows, cols=cols)
+        return oracle.attention_head(Q[b, h], K[b, h], V[b, h], dO[b, h], causal, scale, rows=part,
+                                     cols=cols, visit=part)
+
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            parts = list(ex.map(one, tasks))
+    out = {}
+    for (hd, part), r in zip(tasks, parts):
+        if part is None:
+            out[hd] = r
+            continue
+        acc = out.setdefault(hd, {"O": [], "L": [], "dQ": [], "dK": 0.0, "dV": 0.0})
+        for key in ("O", "L", "dQ"):
+            acc[key].append(r[key])
+        acc["dK"] = acc["dK"] + r["dK"]
+        acc["dV"] = acc["dV"] + r["dV"]
+    for hd, acc in out.items():
+        if isinstance(acc["O"], list):
+            for key in ("O", "L", "dQ"):
+                acc[key] = np.concatenate(acc[key])
+    return out
+
+
+def rounding_floor(res, refs, heads, rows=None):
+    """max|O_bf16 - O_ref| of the kernel's bf16 O beside max|RNE(O_ref) -
+    O_ref|, the error that rounding the exact result to bf16 leaves by
+    itself, over the given heads."""
+    got = f64(res["O"])
+    e_bf16 = floor = 0.0
+    for b, h in heads:
+        ref = refs[(b, h)]["O"]
+        g = got[b, h] if rows is None else got[b, h][rows]
+        rne = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+        e_bf16 = max(e_bf16, float(np.abs(g - ref).max()))
+        floor = max(floor, float(np.abs(rne - ref).max()))
+    return {"max_err_bf16_O": e_bf16, "max_err_RNE_of_exact_O": floor}
+
+
+def report(tag, values):
+    """Print a parity figure and append it to $PARITY_REPORT (JSON lines)."""
+    import json
+    line = {"case": tag, **{k: (float(v) if isinstance(v, (float, np.floating)) else v)
+                            for k, v in values.items()}}
+    print("[parity]", json.dumps(line))
+    path = os.environ.get("PARITY_REPORT")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(line) + "\n")
+
+
 def check_heads(res, q, k, v, do, causal, dtype, heads, scale=None, grads=True, rows=None,
-                cols=None, tag=""):
+                cols=None, tag="", refs=None):
     """Compare the given (b, h) heads of a run with the oracle. rows / cols
     optionally restrict the compared query rows (O, L, dQ) and key rows
-    (dK, dV). Returns a dict of the worst errors."""
+    (dK, dV). refs: oracle results by head, computed here when not given.
+    Returns a dict of the worst errors."""
     tol = TOL[dtype]
     worst = {}
     Q, K, V, dO = f64(q), f64(k), f64(v), f64(do)
+    if refs is None:
+        refs = oracle_heads(Q, K, V, dO if grads else None, causal, heads, scale, rows, cols)
     for b, h in heads:
-        ref = oracle.attention_head(Q[b, h], K[b, h], V[b, h], dO[b, h] if grads else None,
-                                    causal, scale, rows=rows, cols=cols)
+        ref = refs[(b, h)]
         ridx = slice(None) if rows is None else rows
         cidx = slice(None) if cols is None else cols
         o_key = "O32" if dtype == "bf16" else "O"

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import exact_tiled_attention_29_amd as fa
-    from parity import check_heads, check_sum_invariants, f64, run
+    from parity import (check_heads, check_sum_invariants, f64, oracle_heads, report, rounding_floor,
+                        run)
 
 
 @pytest.fixture(autouse=True)
@@ -42,23 +43,32 @@ def test_tiny_f32(name):
     check_heads(res, q, k, v, do, w.causal, "f32", [(0, 0)], tag=name)
 
 
-def test_self_b4h16_n1024_d64():
-    w = WORKLOADS["self_b4h16_n1024_d64"]
+def _workload_parity(name, heads=None, rows=None, cols=None):
+    """Run a workload at full size and compare the given heads (default all)
+    with the oracle; report the worst errors and, for bf16, the kernel's
+    bf16 O error beside the error that rounding the exact O to bf16 leaves."""
+    w = WORKLOADS[name]
     q, k, v, do = make_inputs(w)
     res = run(q, k, v, do, w.causal)
-    heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
-    worst = check_heads(res, q, k, v, do, w.causal, "bf16", heads, tag=w.name)
-    print(w.name, worst)
+    heads = heads or [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    refs = oracle_heads(f64(q), f64(k), f64(v), f64(do), w.causal, heads, rows=rows, cols=cols)
+    worst = check_heads(res, q, k, v, do, w.causal, w.dtype, heads, rows=rows, cols=cols, tag=name,
+                        refs=refs)
+    fig = dict(worst)
+    if w.dtype == "bf16":
+        fig.update(rounding_floor(res, refs, heads, rows))
+    report(f"{name} ({len(heads)} heads)", fig)
+    return res, q, k, v, do, w
+
+
+def test_self_b4h16_n1024_d64():
+    res, q, k, v, do, w = _workload_parity("self_b4h16_n1024_d64")
     check_sum_invariants(res, do, "bf16", w.name)
 
 
 def test_self_b2h32_n4096_d128_causal():
-    w = WORKLOADS["self_b2h32_n4096_d128_causal"]
-    q, k, v, do = make_inputs(w)
-    res = run(q, k, v, do, w.causal)
-    heads = [(0, 0), (0, 21), (1, 9), (1, 31)]
-    worst = check_heads(res, q, k, v, do, w.causal, "bf16", heads, tag=w.name)
-    print(w.name, worst)
+    # every one of the 64 heads, element by element
+    res, q, k, v, do, w = _workload_parity("self_b2h32_n4096_d128_causal")
     check_sum_invariants(res, do, "bf16", w.name)
 
 
@@ -72,9 +82,22 @@ def test_long_b1h8_n32768_d128_causal():
     rng = np.random.default_rng(0)
     rows = np.unique(np.concatenate([edge, rng.integers(0, n, 48)]))
     cols = np.unique(np.concatenate([edge, rng.integers(0, n, 48)]))
-    worst = check_heads(res, q, k, v, do, w.causal, "bf16", [(0, 5)], rows=rows, cols=cols,
-                        tag=w.name)
-    print(w.name, worst)
+    Q, K, V, dO = f64(q), f64(k), f64(v), f64(do)
+    # O, L and dQ on the sampled rows of all 8 heads (the oracle visits only those rows)
+    heads = [(0, h) for h in range(8)]
+    no_cols = np.array([], dtype=np.int64)
+    refs = oracle_heads(Q, K, V, dO, w.causal, heads, rows=rows, cols=no_cols)
+    worst = check_heads(res, q, k, v, do, w.causal, "bf16", heads, rows=rows, cols=no_cols,
+                        tag=w.name + " rows", refs=refs)
+    fig = dict(worst)
+    fig.update(rounding_floor(res, refs, heads, rows))
+    report(f"{w.name} (sampled rows of 8 heads)", fig)
+    # every row (O, L, dQ) and sampled key rows (dK, dV) of two heads
+    heads2 = [(0, 2), (0, 5)]
+    refs2 = oracle_heads(Q, K, V, dO, w.causal, heads2, cols=cols)
+    worst2 = check_heads(res, q, k, v, do, w.causal, "bf16", heads2, cols=cols, tag=w.name + " keys",
+                         refs=refs2)
+    report(f"{w.name} (all rows, sampled keys of 2 heads)", worst2)
     check_sum_invariants(res, do, "bf16", w.name)
 
 
@@ -116,12 +139,8 @@ def test_long_forward_only_rows_all_heads():
 
 
 def test_cross_b8h12_q1000_k3000_d64():
-    w = WORKLOADS["cross_b8h12_q1000_k3000_d64"]
-    q, k, v, do = make_inputs(w)
-    res = run(q, k, v, do, w.causal)
-    heads = [(0, 0), (2, 5), (4, 11), (7, 3), (7, 11)]
-    worst = check_heads(res, q, k, v, do, w.causal, "bf16", heads, tag=w.name)
-    print(w.name, worst)
+    # every one of the 96 heads, element by element
+    res, q, k, v, do, w = _workload_parity("cross_b8h12_q1000_k3000_d64")
     check_sum_invariants(res, do, "bf16", w.name)
 
 
@@ -359,6 +378,21 @@ def test_autograd_wrapper():
     res = {"O": o.detach().cpu(), "L": fa.forward(qg.detach(), kg.detach(), vg.detach(), True)[1].cpu(),
            "dQ": qg.grad.cpu(), "dK": kg.grad.cpu(), "dV": vg.grad.cpu()}
     check_heads(res, q, k, v, do, True, "f32", [(0, 0), (0, 1)], tag="autograd")
+
+
+def test_autograd_wrapper_bf16():
+    # the autograd wrapper on bf16 inputs (the configuration the metric
+    # times), gradients against the oracle at the bf16 bar
+    w = workloads.custom(2, 3, 300, 300, 128, "bf16", True)
+    q, k, v, do = make_inputs(w, seed=9)
+    qg, kg, vg = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention(qg, kg, vg, True)
+    o.backward(do.cuda())
+    o32, l = fa.forward(qg.detach(), kg.detach(), vg.detach(), True, o_dtype=torch.float32)
+    res = {"O": o.detach().cpu(), "O32": o32.cpu(), "L": l.cpu(), "L32": l.cpu(),
+           "dQ": qg.grad.cpu(), "dK": kg.grad.cpu(), "dV": vg.grad.cpu()}
+    assert qg.grad.dtype == torch.bfloat16
+    check_heads(res, q, k, v, do, True, "bf16", [(0, 0), (1, 2)], tag="autograd bf16")
 
 
 def test_scale_argument():
