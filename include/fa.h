@@ -122,6 +122,10 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
  * 256-byte aligned, owned by the caller, contents on entry ignored. Calls
  * that overlap in time must not share a workspace.
  * Results are deterministic: the same inputs give bitwise the same outputs.
+ * Accuracy (bf16): dS is rounded to bf16 for the dQ and dK products; dQ's
+ * error relative to each row's norm was about 2.4e-3 (median) at every
+ * context length measured, 32K to 512K keys (causal, d = 128): it does not
+ * grow with the number of keys summed.
  */
 int fa_bwd(const void* q, const void* k, const void* v,
            const void* o, int o_dtype, const float* lse, const void* d_o,

@@ -81,7 +81,7 @@ def test_counter_lookup_needs_matching_sources(tmp_path, monkeypatch):
 
 def test_summary_lookups_on_the_committed_profiles():
     # the committed summaries name every bench kernel (when they match the sources)
-    if bench.counter_from_summary("fwd_bf16", "MfmaUtil") is None:
+    if bench.counter_from_summary(bench.KERNEL_KEYS["fwd"], "MfmaUtil") is None:
         pytest.skip("committed counter summary predates the kernel sources")
     for key in bench.KERNEL_KEYS.values():
         assert bench.counter_from_summary(key, "MfmaUtil") is not None, key
