@@ -558,6 +558,8 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     dinfo = device_info()
     dinfo["torch_multi_processor_count"] = props.multi_processor_count
+    dinfo["torch_name"] = props.name
+    dinfo["gcn_arch"] = getattr(props, "gcnArchName", None)
     log(f"[bench] device {dinfo.get('name') or props.name}: {dinfo['rocminfo_compute_units']} CUs, "
         f"max clock {dinfo['rocminfo_max_clock_mhz']} MHz (rocminfo)")
 

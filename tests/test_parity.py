@@ -121,8 +121,9 @@ def test_very_long_context_256k():
 def test_dq_error_does_not_grow_with_context(n):
     # dQ sums dS K over every visible key with dS rounded to bf16 for the
     # MFMA. Measured row by row, its relative error stays at about 2.4e-3
-    # (median) from 32K to 512K keys; the check here is the workloads' bar,
-    # max error over max|dQ| of 96 sampled rows, at up to 2^19 tokens.
+    # (median) from 32K to 512K keys; the checks here are the workloads' bar,
+    # max error over max|dQ| of 96 sampled rows, at up to 2^19 tokens, and a
+    # median row error of at most 5e-3.
     w = workloads.custom(1, 1, n, n, 128, "bf16", True)
     q, k, v, do = make_inputs(w, seed=11)
     res = run(q, k, v, do, True)
@@ -132,9 +133,15 @@ def test_dq_error_does_not_grow_with_context(n):
     ref = oracle_heads(Q, K, V, dO, True, [(0, 0)], rows=rows, cols=np.array([], dtype=np.int64))[(0, 0)]
     got = f64(res["dQ"][0, 0])[rows]
     err = float(np.abs(got - ref["dQ"]).max() / np.abs(ref["dQ"]).max())
-    row_rel = np.linalg.norm(got - ref["dQ"], axis=1) / np.linalg.norm(ref["dQ"], axis=1)
-    report(f"dQ error n={n}", {"dQ": err, "dQ_row_relative_median": float(np.median(row_rel))})
+    # row 0 sees key 0 alone, its softmax row is the constant 1 and its dQ is
+    # exactly zero (checked by the max error above): no relative error there
+    norm = np.linalg.norm(ref["dQ"], axis=1)
+    live = norm > 0
+    row_rel = np.linalg.norm(got - ref["dQ"], axis=1)[live] / norm[live]
+    median = float(np.median(row_rel))
+    report(f"dQ error n={n}", {"dQ": err, "dQ_row_relative_median": median})
     assert err <= 2e-2
+    assert median <= 5e-3
 
 
 def test_million_token_forward():
