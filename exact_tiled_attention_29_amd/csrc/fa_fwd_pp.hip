@@ -128,6 +128,21 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
         const unsigned boff = ((unsigned)(ks + row) * D + 8u * (unsigned)(pc ^ tile_swz<D>(row))) * 2u;
         load_lds16(rs, (int)(valid ? boff : 0x80000000u), dst + 512 * b);
     };
+    // The same copy during the loop, where this wave always copies chunks
+    // 4c + sub: the lane's part of the offset is computed once (cpart[c]),
+    // and the tile's part is a wave-uniform base, 0x80000000 for an invalid
+    // copy, so each chunk costs one vector add.
+    unsigned cpart[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int p = 64 * (4 * c + sub) + lane;
+        const int row = p / (D / 8), pc = p % (D / 8);
+        cpart[c] = ((unsigned)row * D + 8u * (unsigned)(pc ^ tile_swz<D>(row))) * 2u;
+    }
+    auto copy_share = [&](__amdgpu_buffer_rsrc_t rs, bf16* dst, int ks, int c, bool valid) __attribute__((always_inline)) {
+        const unsigned base = valid ? (unsigned)ks * D * 2u : 0x80000000u;
+        load_lds16(rs, (int)(base + cpart[c]), dst + 512 * (4 * c + sub));
+    };
     // One tensor tile copied by all eight waves.
     auto copy_by_all = [&](__amdgpu_buffer_rsrc_t rs, bf16* dst, int ks) __attribute__((always_inline)) {
 #pragma unroll
@@ -136,6 +151,13 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
 
     // Per-lane LDS byte offsets (see fa_fwd.hip): K rows r (+32 for the second
     // 32-key block), V transpose reads rows 4g + s16/4 + 8h (+16c).
+    // A read's immediate offset reaches 64 KB past its address register. At
+    // d = 128 the eight stages take 128 KB and the V stages lie past the
+    // first 64 KB, so the V offsets carry a bias of 64 KB that each read
+    // takes off again: the stage's address minus the bias then fits the
+    // immediate, instead of costing an add per read. (Any placement of the
+    // stages stays correct; only the folding depends on it.)
+    constexpr int kVBias = 8 * TILE * 2 > 65536 ? 4 * TILE * 2 : 0;
     int soff[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) soff[kk] = 2 * tile_off<D>(r, 16 * kk + 8 * g);
@@ -144,7 +166,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            troff[db][h] = 2 * tile_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * half + 4 * (s16 & 3));
+            troff[db][h] = 2 * tile_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * half + 4 * (s16 & 3)) + kVBias;
     auto launder = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(soff[kk]));
@@ -205,7 +227,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
                 op[i % (kLook + 1)] = *(const bf16x8*)at(Kb, soff[kk] + kb * 32 * D * 2);
             } else {
                 const int c = j / NDB, db = j % NDB;
-                const int cb = c * 16 * D * 2;
+                const int cb = c * 16 * D * 2 - kVBias;
                 op[i % (kLook + 1)] = concat(lds_read_tr(at(Vb, troff[db][0] + cb)),
                                              lds_read_tr(at(Vb, troff[db][1] + cb)));
             }
@@ -228,7 +250,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
             }
 #pragma unroll
             for (int c = 0; c < CPW; ++c)
-                if (i == copy_slot(c)) copy_chunk(crs, cdst, cks, 4 * c + sub, cvalid);
+                if (i == copy_slot(c)) copy_share(crs, cdst, cks, c, cvalid);
         }
         // Pin the order: the reads of slot i + kLook and any copy chunk
         // follow the MFMA of slot i (one ds_read_b128 for a K operand, two
@@ -368,7 +390,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
         // accumulators through a second register set)
         if (t > wtiles && cvalid) {
 #pragma unroll
-            for (int c = 0; c < CPW; ++c) copy_chunk(crs, cdst, (t + 2) * kPPBC, 4 * c + sub, true);
+            for (int c = 0; c < CPW; ++c) copy_share(crs, cdst, (t + 2) * kPPBC, c, true);
         }
         return t <= wtiles || cvalid;
     };
