@@ -360,7 +360,19 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
         }
     };
 
-    // Prologue: tiles 0 and 1 by all waves.
+    // Prologue: tiles 0 and 1 by all waves. Step 0's matrix half-step runs
+    // O += V P on V stage 3 with P = 0 before any tile has landed there, and
+    // LDS keeps whatever an earlier workgroup left (an fp32 +inf from the
+    // backward's padded rows reads as a bf16 +inf): 0 times Inf or NaN would
+    // make O NaN, so stage 3 starts as zeros.
+    {
+        constexpr int N16 = TILE * 2 / 16;   // 16-byte words of a stage
+#pragma unroll
+        for (int i = 0; i < (N16 + kPPThreads - 1) / kPPThreads; ++i) {
+            const int w = i * kPPThreads + tid;
+            if (w < N16) *(bf16x8*)(Vs3 + 8 * w) = zero_bf16x8();
+        }
+    }
     copy_by_all(krs, Ks0, 0);
     copy_by_all(vrs, Vs0, 0);
     if (ntiles > 1) {

@@ -45,10 +45,14 @@ def run(q, k, v, do, causal, scale=None, backward=True):
     o32, l32 = fa.forward(qg, kg, vg, causal, scale, o_dtype=torch.float32)
     o, l = fa.forward(qg, kg, vg, causal, scale)
     res = {"O32": o32.cpu(), "O": o.cpu(), "L": l.cpu(), "L32": l32.cpu()}
+    # every head, also those the oracle does not see: O is finite (a row
+    # that sees no key gives 0)
+    assert torch.isfinite(res["O32"]).all() and torch.isfinite(res["O"]).all(), "non-finite O"
     if backward:
         dq, dk, dv = fa.backward(qg, kg, vg, o, l, dog, causal, scale)
         torch.cuda.synchronize()
         res.update(dQ=dq.cpu(), dK=dk.cpu(), dV=dv.cpu())
+        assert all(torch.isfinite(res[n]).all() for n in ("dQ", "dK", "dV")), "non-finite gradient"
     del qg, kg, vg, dog
     return res
 
