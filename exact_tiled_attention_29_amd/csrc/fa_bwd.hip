@@ -273,7 +273,6 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     auto rows_times_keys = [&](const bf16* Tb, f32x16& acc_s, auto&& extra, auto nv, const f32x16& init) {
         constexpr int NV = decltype(nv)::value;
         __builtin_amdgcn_sched_barrier(0);
-        acc_s = init;
         bf16x8 a[kLookS + 1];
 #pragma unroll
         for (int kk = 0; kk < kLookS && kk < KK; ++kk) a[kk] = *(const bf16x8*)at(Tb, soff[kk]);
@@ -281,7 +280,8 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         for (int kk = 0; kk < KK; ++kk) {
             if (kk + kLookS < KK)
                 a[(kk + kLookS) % (kLookS + 1)] = *(const bf16x8*)at(Tb, soff[kk + kLookS]);
-            acc_s = mfma32(a[kk % (kLookS + 1)], kv[kk], acc_s);
+            // the first k-step reads init directly (no copy into acc_s)
+            acc_s = mfma32(a[kk % (kLookS + 1)], kv[kk], kk == 0 ? init : acc_s);
             extra(kk);
         }
         __builtin_amdgcn_sched_group_barrier(kDsRead, kLookS < KK ? kLookS : KK, 0);
@@ -381,14 +381,14 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                                              lds_read_tr(at(T2, troff[db][1] + cb)));
             }
         };
-        acc1 = init1;
 #pragma unroll
         for (int i = 0; i < kLook; ++i) load(i);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             if (i + kLook < NS) load(i + kLook);
             if (i < KK) {
-                acc1 = mfma32(op[i % (kLook + 1)], kv[i], acc1);
+                // the first product reads init1 directly (no copy into acc1)
+                acc1 = mfma32(op[i % (kLook + 1)], kv[i], i == 0 ? init1 : acc1);
                 extra1(i);
             } else {
                 const int j = i - KK;
@@ -502,12 +502,18 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                 for (int v = 0; v < 16; ++v) x[v] = nd[v];
                 return x;
             };
-            f32x16 dp_c;
-            rows_times_keys(do_of(Sl0), dp_c, noop, nv0, neg_d_of(Sl0));
+            // dP - D alternates between two register sets (dp_x, dp_y): a
+            // step forms dS from one and writes the next tile's dP into the
+            // other, which is dead at that point. (With one loop-carried set
+            // the compiler put the new dP elsewhere and copied it back after
+            // every step.)
+            f32x16 dp_x, dp_y;
+            rows_times_keys(do_of(Sl0), dp_x, noop, nv0, neg_d_of(Sl0));
             // Step for tile t: dS = P * (dP - D) of tile t-1 (from wave A's
-            // P), dP - D of tile t, then dK of tile t-1. The dS work runs
-            // while wave A of the same SIMD keeps the matrix core busy.
-            auto step = [&](bf16* Sc, bf16* Sp, bf16* Sf, int t) {
+            // P, dP - D in dp_in), dP - D of tile t (into dp_out), then dK
+            // of tile t-1. The dS work runs while wave A of the same SIMD
+            // keeps the matrix core busy.
+            auto step = [&](bf16* Sc, bf16* Sp, bf16* Sf, int t, const f32x16& dp_in, f32x16& dp_out) {
                 copies_barrier();  // tile t landed; P of tile t-1 written
                 if (t + 1 < nqt) issue_tile(Sf, t + 1);
                 launder_offsets();
@@ -516,22 +522,28 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                 read_p(Sp, p);
                 bf16x8 dsa[2];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * dp_c[v]);
-                stream(do_of(Sc), dp_c, nd, q_of(Sp), dsa, none, nv0, noop, nv0, noop, nv0);
+                for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * dp_in[v]);
+                stream(do_of(Sc), dp_out, nd, q_of(Sp), dsa, none, nv0, noop, nv0, noop, nv0);
             };
-            for (int t = t_begin + 1; t < nqt; t += 3) {
-                step(Sl1, Sl0, Sl2, t);
-                if (t + 1 < nqt) step(Sl2, Sl1, Sl0, t + 1);
-                if (t + 2 < nqt) step(Sl0, Sl2, Sl1, t + 2);
+            // Unrolled by six: three ring slots times two dP sets.
+            for (int t = t_begin + 1; t < nqt; t += 6) {
+                step(Sl1, Sl0, Sl2, t, dp_x, dp_y);
+                if (t + 1 < nqt) step(Sl2, Sl1, Sl0, t + 1, dp_y, dp_x);
+                if (t + 2 < nqt) step(Sl0, Sl2, Sl1, t + 2, dp_x, dp_y);
+                if (t + 3 < nqt) step(Sl1, Sl0, Sl2, t + 3, dp_y, dp_x);
+                if (t + 4 < nqt) step(Sl2, Sl1, Sl0, t + 4, dp_x, dp_y);
+                if (t + 5 < nqt) step(Sl0, Sl2, Sl1, t + 5, dp_y, dp_x);
             }
             copies_barrier();  // P of the last tile written
             bf16* Sl = s_last == 0 ? Sl0 : (s_last == 1 ? Sl1 : Sl2);
             launder_offsets();
+            // the last tile's dP - D: in dp_x after an even number of steps
+            const bool in_x = ((t_last - t_begin) & 1) == 0;
             float p[16];
             read_p(Sl, p);
             bf16x8 dsa[2];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * dp_c[v]);
+            for (int v = 0; v < 16; ++v) dsa[v >> 3][v & 7] = to_bf16(p[v] * (in_x ? dp_x[v] : dp_y[v]));
             keys_times_tile(q_of(Sl), dsa, noop, nv0);
         }
     }
