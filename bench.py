@@ -29,6 +29,8 @@ Prints one JSON line (the last line of stdout). For the headline workload
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-configs] [--no-power]
   python bench.py --shape BxHxNQxNKxD [--mask none|top_left|bottom_right]   # any bf16 shape
   python bench.py --rows [--rows-shape RxC]   # standalone row softmax kernel (HBM roofline)
+  python bench.py --io [--io-n N]             # fused vs materialising forward, one head (page 1, section 4)
+  python bench.py --summarize-io DIR --summary-out F   # HBM bytes per call of both forwards
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --summary-out F   # HBM bytes per kernel
   python bench.py --summarize-stats DIR --summary-out F                  # kernel durations
 """
@@ -50,6 +52,11 @@ METRIC = "attention TFLOP/s fwd+bwd (bf16, causal, n=4096, d=128); % MFMA peak"
 CSRC = os.path.join(ROOT, "exact_tiled_attention_29_amd", "csrc")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_self_b2h32_n4096_d128_causal.txt")
 SQ_SUMMARY = os.path.join(ROOT, "profiles", "sq_counters_self_b2h32_n4096_d128_causal.txt")
+IO_SUMMARY = os.path.join(ROOT, "profiles", "io_forward_h1_d128_bf16.txt")
+IO_SIZES = (1024, 4096, 16384, 65536)
+IO_D = 128
+IO_SRAM_ELEMS = 100 * 1024 // 2   # the pages' M: about 100 KB of on-chip memory, in bf16 elements
+FUSED_KEYS = ("fwd_pp_kernel", "fwd_bf16_kernel")
 # Substrings of the bench kernels' mangled names in the rocprofv3 summaries.
 KERNEL_KEYS = {"fwd": "fwd_pp_kernel", "bwd_pre": "bwd_pre_kernel", "bwd_dkdv": "bwd_dkdv",
                "bwd_dq": "bwd_dq_kernel"}
@@ -276,6 +283,180 @@ def oracle_sample(w):
 # --------------------------------------------------------------------------
 # Standalone row softmax / logsumexp kernel
 # --------------------------------------------------------------------------
+
+# --------------------------------------------------------------------------
+# Page 1 ("05_flash_attention.py"), section 4, measured: one head, bf16,
+# d = 128, the fused forward beside the materialising one
+# --------------------------------------------------------------------------
+
+def io_inputs(n, dev):
+    """Seeded Q, K, V of one head (n x 128, bf16) on the device, and the
+    materialising path's operands prepared on the host: scale * Q (bf16)
+    and K^T (contiguous), so that path's calls run only its three kernels."""
+    import math
+    import torch
+    import workloads
+    w = workloads.custom(1, 1, n, n, IO_D, "bf16", False, name=f"io_n{n}")
+    q, k, v, _ = workloads.make_inputs(w, seed=0)
+    scale = 1.0 / math.sqrt(IO_D)
+    qs = (q[0, 0].float() * scale).to(torch.bfloat16)
+    kt = k[0, 0].t().contiguous()
+    up = lambda t: t.contiguous().to(dev)  # noqa: E731
+    return up(q), up(k), up(v), up(qs), up(kt), up(v[0, 0])
+
+
+def materialising_forward(qs, kt, v):
+    """Standard attention as page 1, section 2 writes it (standard_attention):
+    S = Q K^T / sqrt(d) and P = softmax(S) are n x n bf16 matrices in HBM
+    (page 1, section 4 counts exactly these two), O = P V. Plain torch ops
+    (hipBLASLt GEMMs, torch's softmax): the comparison baseline of the IO
+    table, not part of the library."""
+    import torch
+    s = torch.mm(qs, kt)
+    p = torch.softmax(s, dim=-1)
+    return torch.mm(p, v)
+
+
+def io_compare(n, calls=10, warmup=2):
+    """Times `calls` calls of each forward (after `warmup`), measures the
+    device memory each allocates beyond its inputs (peak), and the largest
+    difference between the two outputs."""
+    import torch
+    import exact_tiled_attention_29_amd as fa
+    dev = torch.device("cuda:0")
+    q, k, v, qs, kt, v2 = io_inputs(n, dev)
+    paths = {"materialising": lambda: materialising_forward(qs, kt, v2),
+             "fused": lambda: fa.forward(q, k, v, False)[0]}
+    out = {"n": n, "d": IO_D}
+    res = {}
+    for name, fn in paths.items():
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        o = fn()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        res[name] = o.float().reshape(n, IO_D)
+        del o
+        for _ in range(max(0, warmup - 1)):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        out[name] = {"ms": _stats([a.elapsed_time(b) for a, b in ev]), "peak_extra_bytes": int(peak)}
+    out["max_abs_diff"] = float((res["fused"] - res["materialising"]).abs().max())
+    # the pages' estimates (page 1, section 4): S and P held as bf16 n x n
+    # matrices against one fp32 vector; 4 n^2 accesses against n^2 d^2 / M
+    out["page_memory_bytes"] = {"materialising": 2 * n * n * 2, "fused": 4 * n}
+    out["page_io_elements"] = {"materialising": 4 * n * n,
+                               "fused": round(n * n * IO_D * IO_D / IO_SRAM_ELEMS)}
+    return out
+
+
+def io_traffic_from_summary(n):
+    """HBM bytes per call of each forward at size n from the committed IO
+    summary (None when absent or older than the kernel sources)."""
+    if not os.path.exists(IO_SUMMARY):
+        return None
+    lines = open(IO_SUMMARY).read().splitlines()
+    if f"source_hash {kernel_source_hash()}" not in lines:
+        return None
+    for line in lines:
+        t = line.split()
+        if len(t) >= 6 and t[0] == "n" and t[2] == "materialising" and int(t[1]) == n:
+            return {"materialising": float(t[3]), "fused": float(t[5])}
+    return None
+
+
+def summarize_io(base_dir, out_path, command, copy_bytes=512 << 20):
+    """HBM bytes per call of both forwards from rocprofv3 --pmc runs of
+    `bench.py --io --io-n N --copy-mib 512`: FETCH_SIZE in base_dir/fN,
+    WRITE_SIZE in base_dir/wN. Both paths run the same number of calls in a
+    process, and the fused path is one kernel per call, so the fused
+    kernel's dispatch count is the number of calls. Kernels named in
+    FUSED_KEYS are the fused path,
+    GEMM and softmax kernels the materialising path, the copy kernel of
+    copy_bytes gives the scale factors, and the remaining kernels (set-up,
+    the comparison of the outputs) are listed but counted for neither."""
+    lines = [f"command: {command}", f"source_hash {kernel_source_hash()}",
+             "bytes per call; FETCH_SIZE and WRITE_SIZE scaled by the copy kernel of "
+             f"{copy_bytes} bytes read and written in the same process"]
+    sizes = [os.path.basename(d)[1:] for d in glob.glob(os.path.join(base_dir, "f*")) if os.path.isdir(d)]
+    for n in sorted(int(x) for x in sizes if x.isdigit()):
+        tot = {}
+        for counter, sub in (("FETCH_SIZE", "f"), ("WRITE_SIZE", "w")):
+            acc = {}
+            for r in _read_counter_csv(os.path.join(base_dir, f"{sub}{n}")):
+                if r.get("Counter_Name") == counter:
+                    acc.setdefault(r.get("Kernel_Name", ""), []).append(float(r["Counter_Value"]) * 1024)
+            copy = [max(v) for k, v in acc.items() if "copy" in k.lower()]
+            scale = copy_bytes / max(copy) if copy else 1.0
+            calls = sum(len(v) for k, v in acc.items() if any(f in k for f in FUSED_KEYS)) or 1
+            for k, v in acc.items():
+                if any(f in k for f in FUSED_KEYS):
+                    path = "fused"
+                elif "Cijk" in k or "gemm" in k.lower() or "softmax" in k.lower():
+                    path = "materialising"
+                else:
+                    path = "other"
+                if path != "other":
+                    tot.setdefault(path, {}).setdefault(counter, 0.0)
+                    tot[path][counter] += sum(v) * scale / calls
+                lines.append(f"  n {n} {counter} {path} kernel {k[:90]!r} dispatches {len(v)} "
+                             f"bytes {sum(v) * scale:.0f}")
+        m = tot.get("materialising", {})
+        f_ = tot.get("fused", {})
+        mb = m.get("FETCH_SIZE", 0.0) + m.get("WRITE_SIZE", 0.0)
+        fb = f_.get("FETCH_SIZE", 0.0) + f_.get("WRITE_SIZE", 0.0)
+        lines.append(f"n {n} materialising {mb:.0f} fused {fb:.0f} ratio {mb / fb if fb else float('nan'):.2f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def bench_io(args):
+    """Page 1, section 4's table (one head, bf16, d = 128), measured: time
+    per call, peak device memory beyond the inputs and, from the committed
+    rocprofv3 summary, HBM bytes per call of the materialising and the
+    fused forward."""
+    import torch
+    import exact_tiled_attention_29_amd as fa
+    fa.load_library()
+    torch.cuda.set_device(0)
+    if args.copy_mib:
+        a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    sizes = [args.io_n] if args.io_n else list(IO_SIZES)
+    entries = []
+    for n in sizes:
+        e = io_compare(n, calls=args.io_calls, warmup=min(2, args.io_calls))
+        e["hbm_bytes_per_call"] = io_traffic_from_summary(n)
+        entries.append(e)
+        m, f = e["materialising"], e["fused"]
+        log(f"[io] n={n}: materialising {m['ms']['median']:.4f} ms, {m['peak_extra_bytes'] / 1e6:.1f} MB; "
+            f"fused {f['ms']['median']:.4f} ms, {f['peak_extra_bytes'] / 1e6:.2f} MB; "
+            f"max|dO| {e['max_abs_diff']:.2e}; HBM bytes {e['hbm_bytes_per_call']}")
+    last = entries[-1]
+    result = {
+        "metric": "forward time, materialising / fused (one head, bf16, d=128)",
+        "value": round(last["materialising"]["ms"]["median"] / last["fused"]["ms"]["median"], 3),
+        "unit": "x", "n_gpus": 1, "steps": args.io_calls, "warmup": 2,
+        "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16)",
+        "config": {"workload": f"io_h1_d{IO_D}_n{last['n']}", "sizes": sizes},
+        "io": entries,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
 
 def bench_rows(args):
     """Times fa_row_softmax (softmax + logsumexp of every row) on a bf16
@@ -510,6 +691,12 @@ def main():
     ap.add_argument("--summary-out", default=PMC_SUMMARY)
     ap.add_argument("--summary-copy-mib", type=int, default=512)
     ap.add_argument("--summary-command", default="", help="command line recorded in a summary")
+    ap.add_argument("--io", action="store_true",
+                    help="fused vs materialising forward, one head, d = 128 (page 1, section 4)")
+    ap.add_argument("--io-n", type=int, default=0, help="one size for --io (default: all)")
+    ap.add_argument("--io-calls", type=int, default=10, help="timed calls per path for --io")
+    ap.add_argument("--summarize-io", metavar="DIR",
+                    help="write the IO summary from DIR/fN (FETCH_SIZE) and DIR/wN (WRITE_SIZE)")
     ap.add_argument("--rows", action="store_true",
                     help="benchmark the standalone row softmax / logsumexp kernel instead")
     ap.add_argument("--rows-shape", default="262144x4096",
@@ -527,6 +714,10 @@ def main():
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.summary_out, args.summary_command)
         return 0
+    if args.summarize_io:
+        summarize_io(args.summarize_io, args.summary_out, args.summary_command,
+                     copy_bytes=args.summary_copy_mib << 20)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -541,6 +732,8 @@ def main():
 
     if args.rows:
         return bench_rows(args)
+    if args.io:
+        return bench_io(args)
 
     if args.shape:
         B, H, NQ, NK, D = (int(x) for x in args.shape.lower().split("x"))

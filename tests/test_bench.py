@@ -176,3 +176,37 @@ def test_rocminfo_parse(monkeypatch):
     info = bench.device_info()
     assert info == {"rocminfo_compute_units": 256, "rocminfo_max_clock_mhz": 2400,
                     "name": "AMD Instinct MI355X"}
+
+
+def test_summarize_io_splits_paths_and_scales(tmp_path, monkeypatch):
+    # FETCH_SIZE of the 512 MiB copy reads half its bytes (scale 2), WRITE_SIZE
+    # all of them; 3 calls per path (three fused dispatches)
+    mib = 1 << 20
+    for n in (1024, 4096):
+        fetch = [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "FETCH_SIZE", "Counter_Value": 512 * 1024 / 2},
+                 {"Kernel_Name": "Cijk_Alik_Bljk_BBS", "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0 * n / 1024},
+                 {"Kernel_Name": "Cijk_Alik_Bljk_BBS", "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0 * n / 1024},
+                 {"Kernel_Name": "cunn_SoftMaxForward", "Counter_Name": "FETCH_SIZE", "Counter_Value": 600.0 * n / 1024},
+                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "FETCH_SIZE", "Counter_Value": 10.0},
+                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "FETCH_SIZE", "Counter_Value": 10.0},
+                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "FETCH_SIZE", "Counter_Value": 10.0},
+                 {"Kernel_Name": "at::native::reduce_kernel", "Counter_Name": "FETCH_SIZE", "Counter_Value": 1e6}]
+        write = [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "WRITE_SIZE", "Counter_Value": 512 * 1024},
+                 {"Kernel_Name": "cunn_SoftMaxForward", "Counter_Name": "WRITE_SIZE", "Counter_Value": 300.0 * n / 1024},
+                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0},
+                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0},
+                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0}]
+        _write_csv(str(tmp_path / "io" / f"f{n}" / "run_counter_collection.csv"), fetch)
+        _write_csv(str(tmp_path / "io" / f"w{n}" / "run_counter_collection.csv"), write)
+    out = tmp_path / "io.txt"
+    bench.summarize_io(str(tmp_path / "io"), str(out), "cmd", copy_bytes=512 * mib)
+    monkeypatch.setattr(bench, "IO_SUMMARY", str(out))
+    t = bench.io_traffic_from_summary(1024)
+    # materialising: fetch (300 + 300 + 600) KiB x 2 + write 300 KiB, over 3 calls;
+    # fused: (30 x 2 + 15) KiB over 3 calls; the reduce kernel counts for neither
+    assert t["materialising"] == (1200 * 2 + 300) * 1024 / 3
+    assert t["fused"] == (30 * 2 + 15) * 1024 / 3
+    assert bench.io_traffic_from_summary(4096)["materialising"] == (4800 * 2 + 1200) * 1024 / 3
+    assert bench.io_traffic_from_summary(2048) is None
+    out.write_text(out.read_text().replace(bench.kernel_source_hash(), "0000000000000000"))
+    assert bench.io_traffic_from_summary(1024) is None
