@@ -6,9 +6,10 @@ tensors, allocates outputs with torch on the GPU and passes raw pointers and
 the current HIP stream. There is no CPU fallback: without the built library
 or without a GPU the calls raise.
 
-The C functions are re-exported under their own names (fa_fwd, fa_bwd,
-fa_bwd_timed, fa_bwd_workspace_bytes, fa_row_softmax, fa_status_str,
-fa_abi_version), taking plain ints for pointers. The tensor-level helpers
+The C functions are re-exported under their own names (fa_fwd, fa_fwd_ws,
+fa_fwd_workspace_bytes, fa_bwd, fa_bwd_timed, fa_bwd_noalloc,
+fa_bwd_workspace_bytes, fa_row_softmax, fa_status_str, fa_abi_version),
+taking plain ints for pointers. The tensor-level helpers
 are forward(), backward(), row_softmax() and the autograd wrapper
 FlashAttention / attention().
 """
@@ -23,7 +24,8 @@ import torch  # imported before libfa.so so the process shares torch's HIP runti
 __all__ = [
     "FA_BF16", "FA_F32", "FA_NO_MASK", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT",
     "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_row_softmax",
+    "fa_fwd", "fa_fwd_ws", "fa_fwd_workspace_bytes",
+    "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_row_softmax",
     "fa_status_str", "fa_abi_version",
     "forward", "backward", "row_softmax", "FlashAttention", "attention",
 ]
@@ -38,7 +40,7 @@ FA_CAUSAL_BOTTOM_RIGHT = 2   # key j visible to query i iff j <= i + n_k - n_q
 
 _STATUS = {0: "FA_OK", 1: "FA_E_NULLPTR", 2: "FA_E_SHAPE", 3: "FA_E_DTYPE", 4: "FA_E_HEADDIM",
            5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP", 8: "FA_E_CAUSAL", 9: "FA_E_SCRATCH"}
-_ABI_VERSION = 3
+_ABI_VERSION = 4
 # bytes of the library's static per-GPU scratch behind fa_bwd_noalloc
 FA_BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
 _SIZE_MAX = (1 << 64) - 1
@@ -69,6 +71,10 @@ def load_library():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
     lib.fa_fwd.restype = i32
+    lib.fa_fwd_ws.argtypes = lib.fa_fwd.argtypes[:-1] + [vp, sz, vp]
+    lib.fa_fwd_ws.restype = i32
+    lib.fa_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.fa_fwd_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
@@ -96,6 +102,16 @@ def load_library():
 def fa_fwd(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype, causal, scale, stream):
     return load_library().fa_fwd(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype,
                                  int(causal), float(scale), stream)
+
+
+def fa_fwd_ws(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype, causal, scale,
+              workspace, workspace_bytes, stream):
+    return load_library().fa_fwd_ws(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype,
+                                    int(causal), float(scale), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, causal):
+    return load_library().fa_fwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, int(causal))
 
 
 def fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype, causal,
@@ -185,7 +201,8 @@ def _event_handle(e) -> int:
     return e.cuda_event
 
 
-def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None):
+def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None, split=True,
+            workspace=None):
     """O, L = attention(q, k, v). q: [B,H,n_q,d]; k, v: [B,H,n_k,d].
 
     causal: False, True (= "top_left": key j visible to query i iff j <= i)
@@ -194,6 +211,12 @@ def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None)
 
     o_dtype defaults to the input dtype; torch.float32 gives the unrounded
     fp32 O for bf16 inputs. Returns (O, L) with L fp32 [B,H,n_q].
+
+    split: when the library asks for a workspace (grids with few query
+    tiles, see fa_fwd_ws), let it split the keys over several workgroups,
+    in `workspace` (a uint8 CUDA tensor of at least
+    fa_fwd_workspace_bytes(...) bytes) or in one allocated here; False
+    always calls fa_fwd.
     """
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
@@ -212,10 +235,24 @@ def forward(q, k, v, causal=False, scale=None, o_dtype=None, out=None, lse=None)
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
     _check(lse, "lse", (B, H, n_q), torch.float32, dev)
     with torch.cuda.device(dev):   # kernels launch on the current device
-        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _code(o_dtype),
-                    lse.data_ptr(), B, H, n_q, n_k, d, dt, _mask_code(causal), scale, _stream(dev))
+        need = fa_fwd_workspace_bytes(B, H, n_q, n_k, d, dt, _mask_code(causal)) if split else 0
+        if need == _SIZE_MAX:
+            need = 0   # rejected arguments: fa_fwd reports why
+        if need:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            _check(workspace, "workspace", tuple(workspace.shape), None, dev)
+            st = fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _code(o_dtype),
+                           lse.data_ptr(), B, H, n_q, n_k, d, dt, _mask_code(causal), scale,
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream(dev))
+            where = "fa_fwd_ws"
+        else:
+            st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _code(o_dtype),
+                        lse.data_ptr(), B, H, n_q, n_k, d, dt, _mask_code(causal), scale, _stream(dev))
+            where = "fa_fwd"
     if st != 0:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, where)
     return out, lse
 
 

@@ -88,7 +88,7 @@ int causal_offset(int causal, int n_q, int n_k) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 3; }
+int fa_abi_version(void) { return 4; }
 
 const char* fa_status_str(int status) {
     switch (status) {
@@ -121,6 +121,39 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, fl
     a.o_f32 = o_dtype == FA_F32; a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
     return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+size_t fa_fwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int dtype, int causal) {
+    bool empty = false;
+    const int o_dtype = dtype == FA_F32 ? FA_F32 : FA_BF16;
+    if (check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, 1.0f, &empty) != FA_OK)
+        return SIZE_MAX;
+    if (empty || dtype != FA_BF16) return 0;
+    fa::FwdArgs a{};
+    a.bh = batch * heads; a.n_q = n_q; a.n_k = n_k; a.d = d;
+    return align_up(fa::fwd_split_workspace_bytes(a, fa::fwd_split_plan(a)));
+}
+
+int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+              int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
+              void* workspace, size_t workspace_bytes, void* stream) {
+    bool empty = false;
+    int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, scale, &empty);
+    if (st != FA_OK) return st;
+    if (empty) return FA_OK;
+    if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
+    fa::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.bh = batch * heads; a.n_q = n_q; a.n_k = n_k; a.d = d;
+    a.causal = causal != FA_NO_MASK; a.coff = causal_offset(causal, n_q, n_k);
+    a.o_f32 = o_dtype == FA_F32; a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype != FA_BF16) return hip_status(fa::launch_fwd_f32(a, s));
+    const fa::FwdSplit sp = fa::fwd_split_plan(a);
+    const size_t need = fa::fwd_split_workspace_bytes(a, sp);
+    if (need == 0) return hip_status(fa::launch_fwd_bf16(a, s));
+    if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
+    return hip_status(fa::launch_fwd_split(a, sp, (float*)workspace, s));
 }
 
 size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int dtype, int causal) {

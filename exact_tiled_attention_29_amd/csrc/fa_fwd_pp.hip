@@ -53,11 +53,17 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
     return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
+// Key split (nsplit > 1): the grid holds nsplit "virtual heads" per head;
+// virtual head bhv = bh * nsplit + s attends head bh's queries to keys
+// [s * kchunk, (s + 1) * kchunk) only and writes its partial result at bhv:
+// O (fp32, normalised over those keys), L from the fp32 probability sum and,
+// in Lb, the same logsumexp taken over the bf16 weights the PV product
+// applied (what the merge weights O by; see fwd_merge_kernel).
 template <int D, bool CAUSAL, bool OF32>
 __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    void* __restrict__ Out, float* __restrict__ Lse,
-    int n_q, int n_k, int coff, int n_qtiles, float scale2) {
+    void* __restrict__ Out, float* __restrict__ Lse, float* __restrict__ Lb,
+    int n_q, int n_k_all, int coff, int n_qtiles, float scale2, int nsplit, int kchunk) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int KK = D / 16;            // MFMA k-steps over d
     constexpr int NDB = D / 32;           // 32-wide d blocks of the output
@@ -83,15 +89,21 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
     const int s16 = lane & 15, half = (lane >> 4) & 1;
     const int grp = wave >> 2, sub = wave & 3;
 
-    int bh, rank;   // rank 0 = last query tile: longest causal work first
-    work_item(blockIdx.x, gridDim.x / n_qtiles, n_qtiles, &bh, &rank);
+    int bhv, rank;   // rank 0 = last query tile: longest causal work first
+    work_item(blockIdx.x, gridDim.x / n_qtiles, n_qtiles, &bhv, &rank);
     const int qt = n_qtiles - 1 - rank;
     const int q0 = qt * kPPRows;
     const int qw = q0 + 32 * (2 * sub + grp);   // this wave's first row
+    // this workgroup's keys: [k_lo, k_lo + n_k) of head bh, with the causal
+    // diagonal moved to those local key indices
+    const int bh = bhv / nsplit;
+    const int k_lo = (bhv - bh * nsplit) * kchunk;
+    const int n_k = max(0, min(n_k_all, k_lo + kchunk) - k_lo);
+    coff -= k_lo;
 
     const bf16* Qh = Q + (size_t)bh * n_q * D;
-    const bf16* Kh = K + (size_t)bh * n_k * D;
-    const bf16* Vh = V + (size_t)bh * n_k * D;
+    const bf16* Kh = K + ((size_t)bh * n_k_all + k_lo) * D;
+    const bf16* Vh = V + ((size_t)bh * n_k_all + k_lo) * D;
 
     // Q rows as MFMA B operands: lane (r, g) holds d = 16*kk + 8*g .. +7.
     bf16x8 qreg[KK];
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
     const int row = qw + r;
     if (row < n_q) {
         const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
-        const size_t obase = ((size_t)bh * n_q + row) * D;
+        const size_t obase = ((size_t)bhv * n_q + row) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -464,8 +476,62 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
                     *(bf16x4*)((bf16*)Out + obase + d0) = pk;
                 }
             }
-        if (g == 0) Lse[(size_t)bh * n_q + row] = kLn2 * (m_ref + fast_log2(l));
+        if (g == 0) {
+            Lse[(size_t)bhv * n_q + row] = kLn2 * (m_ref + fast_log2(l));
+            if (Lb) Lb[(size_t)bhv * n_q + row] = kLn2 * (m_ref + fast_log2(lb));
+        }
     }
+}
+
+// Merge of the key-split partials of one row (one wave per row, four rows
+// per workgroup): with the partial logsumexps L_s (fp32 probability sums)
+// and B_s (bf16 weight sums), L = log sum_s exp(L_s) and
+// O = sum_s exp(B_s - B) O_s, B = log sum_s exp(B_s) (the online-softmax
+// merge of page 1, section 2, applied across workgroups instead of key
+// tiles). Weighting by the bf16 sums keeps O the quotient of the bf16-weighted
+// sum of V rows by the sum of those weights, as without the split. A row
+// with no visible key in any split gets O = 0, L = -inf.
+template <int D, bool OF32>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(
+    const float* __restrict__ po, const float* __restrict__ pl, const float* __restrict__ plb,
+    void* __restrict__ Out, float* __restrict__ Lse, long long rows, int n_q, int nsplit) {
+    constexpr int PL = D / 64;   // values per lane
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const long long bh = row / n_q;
+    const int r = (int)(row - bh * n_q);
+    const size_t first = (size_t)bh * nsplit * n_q + r;   // split s at first + s * n_q
+    float ml = kNegInf, mb = kNegInf;
+    for (int s = 0; s < nsplit; ++s) {
+        ml = fmaxf(ml, pl[first + (size_t)s * n_q]);
+        mb = fmaxf(mb, plb[first + (size_t)s * n_q]);
+    }
+    float sl = 0.0f, sb = 0.0f;
+    if (mb != kNegInf) {
+        for (int s = 0; s < nsplit; ++s) {
+            sl += fast_exp2((pl[first + (size_t)s * n_q] - ml) * kLog2e);
+            sb += fast_exp2((plb[first + (size_t)s * n_q] - mb) * kLog2e);
+        }
+    }
+    float acc[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) acc[i] = 0.0f;
+    if (mb != kNegInf) {
+        const float b = mb + kLn2 * fast_log2(sb);
+        for (int s = 0; s < nsplit; ++s) {
+            const float w = fast_exp2((plb[first + (size_t)s * n_q] - b) * kLog2e);
+            const float* o = po + (first + (size_t)s * n_q) * D;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) acc[i] = fmaf(w, o[64 * i + lane], acc[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        if (OF32) ((float*)Out)[(size_t)row * D + 64 * i + lane] = acc[i];
+        else ((bf16*)Out)[(size_t)row * D + 64 * i + lane] = to_bf16(acc[i]);
+    }
+    if (lane == 0) Lse[row] = mb != kNegInf ? ml + kLn2 * fast_log2(sl) : kNegInf;
 }
 
 template <int D, bool CAUSAL, bool OF32>
@@ -474,8 +540,30 @@ hipError_t launch_pp(const FwdArgs& a, hipStream_t st) {
     const long long nwg = (long long)a.bh * n_qtiles;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, OF32>), dim3((unsigned)nwg), dim3(kPPThreads), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o, a.lse,
-                       a.n_q, a.n_k, a.coff, n_qtiles, a.scale * kLog2e);
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o, a.lse, (float*)nullptr,
+                       a.n_q, a.n_k, a.coff, n_qtiles, a.scale * kLog2e, 1, a.n_k);
+    return hipGetLastError();
+}
+
+// Key-split forward: partials of every split into the workspace (fp32 O,
+// then L, then the bf16-weight logsumexp), then the merge into O and L.
+template <int D, bool CAUSAL, bool OF32>
+hipError_t launch_pp_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st) {
+    const int n_qtiles = (a.n_q + kPPRows - 1) / kPPRows;
+    const long long nwg = (long long)a.bh * sp.nsplit * n_qtiles;
+    const long long rows = (long long)a.bh * a.n_q;
+    if (nwg > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
+    float* po = ws;
+    float* pl = po + (size_t)sp.nsplit * rows * D;
+    float* plb = pl + (size_t)sp.nsplit * rows;
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, true>), dim3((unsigned)nwg), dim3(kPPThreads), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (void*)po, pl, plb,
+                       a.n_q, a.n_k, a.coff, n_qtiles, a.scale * kLog2e, sp.nsplit, sp.kchunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_merge_kernel<D, OF32>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                       (const float*)po, (const float*)pl, (const float*)plb, a.o, a.lse, rows, a.n_q,
+                       sp.nsplit);
     return hipGetLastError();
 }
 
@@ -484,6 +572,15 @@ hipError_t dispatch_pp(const FwdArgs& a, hipStream_t st) {
     if (a.causal)
         return a.o_f32 ? launch_pp<D, true, true>(a, st) : launch_pp<D, true, false>(a, st);
     return a.o_f32 ? launch_pp<D, false, true>(a, st) : launch_pp<D, false, false>(a, st);
+}
+
+template <int D>
+hipError_t dispatch_pp_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st) {
+    if (a.causal)
+        return a.o_f32 ? launch_pp_split<D, true, true>(a, sp, ws, st)
+                       : launch_pp_split<D, true, false>(a, sp, ws, st);
+    return a.o_f32 ? launch_pp_split<D, false, true>(a, sp, ws, st)
+                   : launch_pp_split<D, false, false>(a, sp, ws, st);
 }
 
 }  // namespace
@@ -512,6 +609,50 @@ hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t st) {
     switch (a.d) {
         case 64: return dispatch_pp<64>(a, st);
         case 128: return dispatch_pp<128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Key split for grids that leave most CUs idle: when the 256-row
+// workgroups would occupy at most half of the CUs and there are at least
+// 2048 keys, split each query tile's keys into the fewest chunks (whole
+// 64-key tiles, at least 256 keys each) whose workgroups fill the CUs in
+// whole rounds (or four or more); failing that, into as many as fill one
+// round. Measured: one head of 4096 (16 workgroups) 1.8x faster split; the
+// cross-attention workload (384 workgroups, 3000 keys) 1.5x slower split in
+// two, and one head of 1024 keys slower too (the merge and the partials
+// cost more than the idle CUs): those stay unsplit. Head dims 64 and 128
+// only; nsplit = 1 means no split.
+FwdSplit fwd_split_plan(const FwdArgs& a) {
+    FwdSplit sp{1, a.n_k};
+    if ((a.d != 128 && a.d != 64) || a.n_k < 2048) return sp;
+    const long long nwg = (long long)a.bh * ((a.n_q + kPPRows - 1) / kPPRows);
+    const int cus = device_cu_count();
+    if (cus <= 0 || 2 * nwg > cus) return sp;
+    const int s_max = a.n_k / 256;
+    auto plan = [&](int s) {
+        const int chunk = ((a.n_k + s - 1) / s + kPPBC - 1) / kPPBC * kPPBC;
+        return FwdSplit{(a.n_k + chunk - 1) / chunk, chunk};
+    };
+    for (int s = 2; s <= s_max && nwg * s <= 8LL * cus; ++s) {
+        const FwdSplit p = plan(s);
+        if (fills_cus(nwg * p.nsplit)) return p;
+    }
+    const long long s_round = (cus + nwg - 1) / nwg;   // one full round
+    const int s = (int)(s_round < s_max ? s_round : s_max);
+    return s >= 2 ? plan(s) : sp;
+}
+
+size_t fwd_split_workspace_bytes(const FwdArgs& a, const FwdSplit& sp) {
+    if (sp.nsplit <= 1) return 0;
+    const size_t rows = (size_t)a.bh * (size_t)a.n_q * (size_t)sp.nsplit;
+    return rows * ((size_t)a.d + 2) * sizeof(float);
+}
+
+hipError_t launch_fwd_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st) {
+    switch (a.d) {
+        case 64: return dispatch_pp_split<64>(a, sp, ws, st);
+        case 128: return dispatch_pp_split<128>(a, sp, ws, st);
         default: return hipErrorInvalidValue;
     }
 }

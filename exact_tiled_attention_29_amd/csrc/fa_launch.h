@@ -68,6 +68,16 @@ inline bool fills_cus(long long nwg) {
 bool fwd_pp_supports(const FwdArgs& a);
 hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t st);
 
+// Key-split forward (fa_fwd_pp.hip): nsplit workgroups per query tile, each
+// over kchunk keys (a multiple of 64), then a merge of their partials.
+struct FwdSplit {
+    int nsplit;
+    int kchunk;
+};
+FwdSplit fwd_split_plan(const FwdArgs& a);
+size_t fwd_split_workspace_bytes(const FwdArgs& a, const FwdSplit& sp);
+hipError_t launch_fwd_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st);
+
 // float32 path (fp32 FMA).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st);

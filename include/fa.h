@@ -95,6 +95,41 @@ int fa_fwd(const void* q, const void* k, const void* v,
            int causal, float scale, void* stream);
 
 /*
+ * Bytes of device workspace that let fa_fwd_ws split the keys of each query
+ * tile over several workgroups for these sizes; 0 when it would not split
+ * (the grid of query tiles already fills the GPU's compute units, or the
+ * head dim is not 64 or 128, or float32, or fewer than 512 keys, or an empty
+ * call). The answer depends on the current device's compute-unit count.
+ * Returns SIZE_MAX for arguments fa_fwd would reject.
+ */
+size_t fa_fwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
+                              int dtype, int causal);
+
+/*
+ * fa_fwd with a workspace: the same arguments, outputs and definition, for
+ * grids with few query tiles (few heads, short query ranges, decoding-like
+ * bottom-right calls). When fa_fwd_workspace_bytes(...) > 0 the keys of each
+ * query tile are split into chunks of whole 64-key tiles, one workgroup per
+ * chunk computes O and L over its keys into the workspace, and a second
+ * kernel merges the chunks row by row: L = ln sum_s exp(L_s), O = sum_s
+ * w_s O_s with w_s = exp(B_s - B), where B_s is the logsumexp of the bf16
+ * weights chunk s applied in its PV product (the rescaling that merges the
+ * running (m, l) of two key tiles on page 1, "05_flash_attention.py",
+ * section 2, applied across workgroups). Otherwise it runs exactly fa_fwd.
+ * Results equal fa_fwd's up to rounding, not bitwise; they are
+ * deterministic.
+ * workspace: device memory of at least fa_fwd_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller, contents on entry ignored; may be
+ * NULL when that size is 0. Too small (or NULL when needed): FA_E_WORKSPACE
+ * with nothing launched. Calls that overlap in time must not share it.
+ */
+int fa_fwd_ws(const void* q, const void* k, const void* v,
+              void* o, int o_dtype, float* lse,
+              int batch, int heads, int n_q, int n_k, int d, int dtype,
+              int causal, float scale,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for these sizes (0 for an empty
  * call). bf16: the fp32 row term -D and L * log2(e), each [B,H,ceil(n_q/32)*32]
  * and 256-byte aligned; float32: D [B,H,n_q]. Returns SIZE_MAX for
@@ -201,10 +236,10 @@ int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float sca
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 
-/* ABI version of this header: 3 (2 added FA_CAUSAL_BOTTOM_RIGHT and
+/* ABI version of this header: 4 (2 added FA_CAUSAL_BOTTOM_RIGHT and
    FA_E_CAUSAL; 3 added fa_bwd_noalloc and FA_E_SCRATCH, and
    fa_bwd_workspace_bytes returns SIZE_MAX instead of 0 for rejected
-   arguments). */
+   arguments; 4 added fa_fwd_workspace_bytes and fa_fwd_ws). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

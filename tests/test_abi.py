@@ -38,8 +38,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc", "fa_bwd_workspace_bytes",
-         "fa_row_softmax", "fa_status_str", "fa_abi_version"])
+        ["fa_fwd", "fa_fwd_ws", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc",
+         "fa_bwd_workspace_bytes", "fa_row_softmax", "fa_status_str", "fa_abi_version"])
 
 
 def test_library_exports_every_header_function(lib):
@@ -52,7 +52,7 @@ def test_library_exports_every_header_function(lib):
 
 
 def test_status_strings(lib):
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
     for code in range(10):
         s = fa.fa_status_str(code)
         assert s and s != "unknown status"
@@ -66,6 +66,13 @@ def fwd(**kw):
     return fa.fa_fwd(**args)
 
 
+def fwd_ws(**kw):
+    args = dict(q=P, k=P, v=P, o=P, o_dtype=BF16, lse=P, batch=1, heads=1, n_q=8, n_k=8, d=64,
+                dtype=BF16, causal=0, scale=0.125, workspace=P, workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_ws(**args)
+
+
 def bwd(**kw):
     args = dict(q=P, k=P, v=P, o=P, o_dtype=BF16, lse=P, d_o=P, dq=P, dk=P, dv=P, batch=1, heads=1,
                 n_q=8, n_k=8, d=64, dtype=BF16, causal=0, scale=0.125, workspace=P,
@@ -74,7 +81,7 @@ def bwd(**kw):
     return fa.fa_bwd(**args)
 
 
-@pytest.mark.parametrize("call", [fwd, bwd])
+@pytest.mark.parametrize("call", [fwd, fwd_ws, bwd])
 def test_validation_codes(lib, call):
     assert call(dtype=7) == DTYPE
     assert call(o_dtype=5) == DTYPE
@@ -151,9 +158,24 @@ def test_noalloc_validation_codes(lib):
 
 def test_empty_forward_is_a_noop(lib):
     # Nothing to compute: returns before any HIP call, pointers untouched.
-    assert fwd(n_q=0, q=None, o=None, lse=None) == OK
-    assert fwd(batch=0, q=None, k=None, v=None, o=None, lse=None) == OK
-    assert fwd(heads=0, n_k=0) == OK
+    for call in (fwd, fwd_ws):
+        assert call(n_q=0, q=None, o=None, lse=None) == OK
+        assert call(batch=0, q=None, k=None, v=None, o=None, lse=None) == OK
+        assert call(heads=0, n_k=0) == OK
+    assert fwd_ws(n_q=0, workspace=None, workspace_bytes=0) == OK
+
+
+def test_forward_workspace_bytes(lib):
+    # SIZE_MAX for what fa_fwd rejects; 0 for empty calls and for the paths
+    # that never split (float32, head dims other than 64 and 128, few keys)
+    assert fa.fa_fwd_workspace_bytes(1, 1, 8, 8, 80, BF16, 0) == REJECTED
+    assert fa.fa_fwd_workspace_bytes(1, 1, 8, 0, 64, BF16, 0) == REJECTED
+    assert fa.fa_fwd_workspace_bytes(1, 1, 8, 8, 64, BF16, 3) == REJECTED
+    assert fa.fa_fwd_workspace_bytes(1, 1, 8, 8, 64, 9, 0) == REJECTED
+    assert fa.fa_fwd_workspace_bytes(0, 1, 8, 8, 64, BF16, 0) == 0
+    assert fa.fa_fwd_workspace_bytes(1, 1, 4096, 4096, 32, F32, 0) == 0
+    assert fa.fa_fwd_workspace_bytes(1, 1, 4096, 4096, 96, BF16, 0) == 0
+    assert fa.fa_fwd_workspace_bytes(1, 1, 4096, 511, 128, BF16, 0) == 0
 
 
 def test_workspace_bytes(lib):

@@ -240,6 +240,73 @@ def test_edge_shapes(B, H, n_q, n_k, d, dtype, causal):
     check_heads(res, q, k, v, do, causal, dtype, heads, tag=str((B, H, n_q, n_k, d, dtype, causal)))
 
 
+# Grids with few query tiles, where fa_fwd_ws splits each tile's keys over
+# several workgroups and merges their partials: one head at 4096 tokens,
+# decoding-like bottom-right calls, ragged key counts, causal n_q != n_k,
+# and rows that see no key in any chunk.
+SPLIT_SHAPES = [
+    (1, 1, 4096, 4096, 128, "bf16", False),
+    (1, 1, 4096, 4096, 128, "bf16", True),
+    (1, 1, 4096, 4096, 64, "bf16", True),
+    (1, 4, 1, 8192, 128, "bf16", "bottom_right"),
+    (2, 8, 16, 4096, 64, "bf16", "bottom_right"),
+    (1, 2, 300, 2100, 128, "bf16", False),
+    (1, 2, 700, 2500, 64, "bf16", True),
+    (1, 2, 3000, 2200, 128, "bf16", "bottom_right"),
+]
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", SPLIT_SHAPES)
+def test_split_forward(B, H, n_q, n_k, d, dtype, causal):
+    mask = {False: 0, True: 1, "bottom_right": 2}[causal]
+    need = fa.fa_fwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask)
+    assert need > 0, "this shape should take the key split"
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
+    q, k, v, do = make_inputs(w, seed=n_q + 3 * n_k)
+    res = run(q, k, v, do, causal)            # forward() splits when asked to
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    tag = "split " + str((B, H, n_q, n_k, d, dtype, causal))
+    check_heads(res, q, k, v, do, causal, dtype, heads, tag=tag)
+    # the unsplit kernel: the same result up to rounding; the split is
+    # deterministic
+    qg, kg, vg = (t.cuda() for t in (q, k, v))
+    o1, l1 = fa.forward(qg, kg, vg, causal, o_dtype=torch.float32, split=False)
+    o2, l2 = fa.forward(qg, kg, vg, causal, o_dtype=torch.float32)
+    o3, l3 = fa.forward(qg, kg, vg, causal, o_dtype=torch.float32)
+    assert torch.equal(o2, o3) and torch.equal(l2, l3)
+    assert torch.equal(o2.cpu(), res["O32"])
+    live = torch.isfinite(l1)
+    assert torch.equal(live, torch.isfinite(l2))
+    assert float((o1 - o2).abs().max()) <= 1e-2
+    assert float((l1[live] - l2[live]).abs().max()) <= 1e-3
+
+
+def test_split_forward_needs_its_workspace():
+    B, H, n_q, n_k, d = 1, 1, 4096, 4096, 128
+    need = fa.fa_fwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, 0)
+    assert need > 0
+    x = torch.zeros(B, H, n_q, d, dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(x, 7.0)
+    lse = torch.empty(B, H, n_q, device="cuda")
+    args = (x.data_ptr(), x.data_ptr(), x.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
+            B, H, n_q, n_k, d, fa.FA_BF16, 0, 0.1)
+    stream = torch.cuda.current_stream().cuda_stream
+    assert fa.fa_fwd_ws(*args, 0, need, stream) == 6            # FA_E_WORKSPACE, nothing launched
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert fa.fa_fwd_ws(*args, ws.data_ptr(), need - 1, stream) == 6
+    torch.cuda.synchronize()
+    assert float(o.float().min()) == 7.0                        # untouched
+    assert fa.fa_fwd_ws(*args, ws.data_ptr(), need, stream) == 0
+    torch.cuda.synchronize()
+    # Q = K = V = 0: every score is 0, O is the mean of V = 0, L = ln n_k
+    assert float(o.float().abs().max()) == 0.0
+    assert float((lse - math.log(n_k)).abs().max()) <= 1e-5
+    # grids that fill most of the CUs, and short key ranges: no split
+    assert fa.fa_fwd_workspace_bytes(2, 32, 4096, 4096, d, fa.FA_BF16, 1) == 0
+    assert fa.fa_fwd_workspace_bytes(8, 12, 1000, 3000, 64, fa.FA_BF16, 0) == 0
+    assert fa.fa_fwd_workspace_bytes(1, 1, 1024, 1024, d, fa.FA_BF16, 0) == 0
+
+
 # Shapes with 1024 (batch, head) pairs, so every forward launch has at least
 # four 256-row workgroups per CU and takes the phase-locked two-group kernel
 # (head dims 64 and 128): ragged tails, n_q != n_k both ways, every mask.
