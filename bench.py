@@ -317,26 +317,43 @@ def materialising_forward(qs, kt, v):
     return torch.mm(p, v)
 
 
-def io_compare(n, calls=10, warmup=2):
+def fa_forward_workspace(n):
+    """Bytes of the key-split workspace the fused forward takes for one head
+    of n x n, d = 128 (0 when it does not split)."""
+    import exact_tiled_attention_29_amd as fa
+    return fa.fa_fwd_workspace_bytes(1, 1, n, n, IO_D, fa.FA_BF16, 0)
+
+
+IO_PATHS = ("materialising", "fused", "fused_split")
+
+
+def io_compare(n, calls=10, warmup=2, paths=IO_PATHS):
     """Times `calls` calls of each forward (after `warmup`), measures the
     device memory each allocates beyond its inputs (peak), and the largest
-    difference between the two outputs."""
+    difference between the outputs. Paths: the materialising forward, the
+    fused forward without the key split (fa_fwd) and with it (fa_fwd_ws,
+    only where the library splits this size)."""
     import torch
     import exact_tiled_attention_29_amd as fa
     dev = torch.device("cuda:0")
     q, k, v, qs, kt, v2 = io_inputs(n, dev)
-    paths = {"materialising": lambda: materialising_forward(qs, kt, v2),
-             "fused": lambda: fa.forward(q, k, v, False)[0]}
-    out = {"n": n, "d": IO_D}
+    fns = {"materialising": lambda: materialising_forward(qs, kt, v2),
+           "fused": lambda: fa.forward(q, k, v, False, split=False)[0],
+           "fused_split": lambda: fa.forward(q, k, v, False)[0]}
+    ws = fa_forward_workspace(n)
+    out = {"n": n, "d": IO_D, "fused_split_workspace_bytes": int(ws)}
     res = {}
-    for name, fn in paths.items():
+    for name in paths:
+        if name == "fused_split" and ws == 0:
+            continue
+        fn = fns[name]
         torch.cuda.synchronize()
         torch.cuda.reset_peak_memory_stats()
         base = torch.cuda.memory_allocated()
         o = fn()
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
-        res[name] = o.float().reshape(n, IO_D)
+        res[name] = o.reshape(n, IO_D)
         del o
         for _ in range(max(0, warmup - 1)):
             fn()
@@ -349,7 +366,11 @@ def io_compare(n, calls=10, warmup=2):
             b.record()
         torch.cuda.synchronize()
         out[name] = {"ms": _stats([a.elapsed_time(b) for a, b in ev]), "peak_extra_bytes": int(peak)}
-    out["max_abs_diff"] = float((res["fused"] - res["materialising"]).abs().max())
+    if "materialising" in res:
+        ref = res["materialising"].float()
+        for name in res:
+            if name != "materialising":
+                out[name]["max_abs_diff_vs_materialising"] = float((res[name].float() - ref).abs().max())
     # the pages' estimates (page 1, section 4): S and P held as bf16 n x n
     # matrices against one fp32 vector; 4 n^2 accesses against n^2 d^2 / M
     out["page_memory_bytes"] = {"materialising": 2 * n * n * 2, "fused": 4 * n}
@@ -360,60 +381,69 @@ def io_compare(n, calls=10, warmup=2):
 
 def io_traffic_from_summary(n):
     """HBM bytes per call of each forward at size n from the committed IO
-    summary (None when absent or older than the kernel sources)."""
+    summary ({} when absent or older than the kernel sources)."""
     if not os.path.exists(IO_SUMMARY):
-        return None
+        return {}
     lines = open(IO_SUMMARY).read().splitlines()
     if f"source_hash {kernel_source_hash()}" not in lines:
-        return None
+        return {}
+    out = {}
     for line in lines:
         t = line.split()
-        if len(t) >= 6 and t[0] == "n" and t[2] == "materialising" and int(t[1]) == n:
-            return {"materialising": float(t[3]), "fused": float(t[5])}
-    return None
+        if len(t) == 5 and t[0] == "n" and int(t[1]) == n and t[3] == "bytes_per_call":
+            out[t[2]] = float(t[4])
+    return out
+
+
+def _io_anchor(path, kernel):
+    """Whether `kernel` runs exactly once per call of `path` (it counts the calls)."""
+    if path == "materialising":
+        return "softmax" in kernel.lower()
+    if path == "fused_split":
+        return "fwd_merge_kernel" in kernel
+    return any(f in kernel for f in FUSED_KEYS)
+
+
+def _io_member(path, kernel):
+    """Whether `kernel` belongs to `path` (set-up and copy kernels do not)."""
+    if path == "materialising":
+        return "Cijk" in kernel or "gemm" in kernel.lower() or "softmax" in kernel.lower()
+    return any(f in kernel for f in FUSED_KEYS) or "fwd_merge_kernel" in kernel
 
 
 def summarize_io(base_dir, out_path, command, copy_bytes=512 << 20):
-    """HBM bytes per call of both forwards from rocprofv3 --pmc runs of
-    `bench.py --io --io-n N --copy-mib 512`: FETCH_SIZE in base_dir/fN,
-    WRITE_SIZE in base_dir/wN. Both paths run the same number of calls in a
-    process, and the fused path is one kernel per call, so the fused
-    kernel's dispatch count is the number of calls. Kernels named in
-    FUSED_KEYS are the fused path,
-    GEMM and softmax kernels the materialising path, the copy kernel of
-    copy_bytes gives the scale factors, and the remaining kernels (set-up,
-    the comparison of the outputs) are listed but counted for neither."""
+    """HBM bytes per call of each forward from rocprofv3 --pmc runs of
+    `bench.py --io --io-n N --io-path PATH --copy-mib 512`, one path per
+    process: FETCH_SIZE in base_dir/fN_PATH, WRITE_SIZE in base_dir/wN_PATH.
+    The copy kernel of copy_bytes gives the counters' scale factors; the
+    path's kernels (GEMMs and softmax; the attention and merge kernels) are
+    summed, and one kernel that runs once per call counts the calls."""
     lines = [f"command: {command}", f"source_hash {kernel_source_hash()}",
              "bytes per call; FETCH_SIZE and WRITE_SIZE scaled by the copy kernel of "
              f"{copy_bytes} bytes read and written in the same process"]
-    sizes = [os.path.basename(d)[1:] for d in glob.glob(os.path.join(base_dir, "f*")) if os.path.isdir(d)]
-    for n in sorted(int(x) for x in sizes if x.isdigit()):
-        tot = {}
+    runs = []
+    for d in glob.glob(os.path.join(base_dir, "f*_*")):
+        if os.path.isdir(d):
+            n, path = os.path.basename(d)[1:].split("_", 1)
+            if n.isdigit() and path in IO_PATHS:
+                runs.append((int(n), path))
+    for n, path in sorted(runs, key=lambda r: (r[0], IO_PATHS.index(r[1]))):
+        total = 0.0
         for counter, sub in (("FETCH_SIZE", "f"), ("WRITE_SIZE", "w")):
             acc = {}
-            for r in _read_counter_csv(os.path.join(base_dir, f"{sub}{n}")):
+            for r in _read_counter_csv(os.path.join(base_dir, f"{sub}{n}_{path}")):
                 if r.get("Counter_Name") == counter:
                     acc.setdefault(r.get("Kernel_Name", ""), []).append(float(r["Counter_Value"]) * 1024)
             copy = [max(v) for k, v in acc.items() if "copy" in k.lower()]
             scale = copy_bytes / max(copy) if copy else 1.0
-            calls = sum(len(v) for k, v in acc.items() if any(f in k for f in FUSED_KEYS)) or 1
+            calls = sum(len(v) for k, v in acc.items() if _io_anchor(path, k)) or 1
             for k, v in acc.items():
-                if any(f in k for f in FUSED_KEYS):
-                    path = "fused"
-                elif "Cijk" in k or "gemm" in k.lower() or "softmax" in k.lower():
-                    path = "materialising"
-                else:
-                    path = "other"
-                if path != "other":
-                    tot.setdefault(path, {}).setdefault(counter, 0.0)
-                    tot[path][counter] += sum(v) * scale / calls
-                lines.append(f"  n {n} {counter} {path} kernel {k[:90]!r} dispatches {len(v)} "
-                             f"bytes {sum(v) * scale:.0f}")
-        m = tot.get("materialising", {})
-        f_ = tot.get("fused", {})
-        mb = m.get("FETCH_SIZE", 0.0) + m.get("WRITE_SIZE", 0.0)
-        fb = f_.get("FETCH_SIZE", 0.0) + f_.get("WRITE_SIZE", 0.0)
-        lines.append(f"n {n} materialising {mb:.0f} fused {fb:.0f} ratio {mb / fb if fb else float('nan'):.2f}")
+                member = _io_member(path, k)
+                if member:
+                    total += sum(v) * scale / calls
+                lines.append(f"  n {n} {path} {counter} {'counted' if member else 'other'} kernel "
+                             f"{k[:90]!r} dispatches {len(v)} bytes {sum(v) * scale:.0f}")
+        lines.append(f"n {n} {path} bytes_per_call {total:.0f}")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -422,8 +452,8 @@ def summarize_io(base_dir, out_path, command, copy_bytes=512 << 20):
 def bench_io(args):
     """Page 1, section 4's table (one head, bf16, d = 128), measured: time
     per call, peak device memory beyond the inputs and, from the committed
-    rocprofv3 summary, HBM bytes per call of the materialising and the
-    fused forward."""
+    rocprofv3 summary, HBM bytes per call of the materialising forward and
+    of the fused forward without and with the key split."""
     import torch
     import exact_tiled_attention_29_amd as fa
     fa.load_library()
@@ -435,19 +465,20 @@ def bench_io(args):
         torch.cuda.synchronize()
         del a, b
     sizes = [args.io_n] if args.io_n else list(IO_SIZES)
+    paths = IO_PATHS if args.io_path == "all" else (args.io_path,)
     entries = []
     for n in sizes:
-        e = io_compare(n, calls=args.io_calls, warmup=min(2, args.io_calls))
+        e = io_compare(n, calls=args.io_calls, warmup=min(2, args.io_calls), paths=paths)
         e["hbm_bytes_per_call"] = io_traffic_from_summary(n)
         entries.append(e)
-        m, f = e["materialising"], e["fused"]
-        log(f"[io] n={n}: materialising {m['ms']['median']:.4f} ms, {m['peak_extra_bytes'] / 1e6:.1f} MB; "
-            f"fused {f['ms']['median']:.4f} ms, {f['peak_extra_bytes'] / 1e6:.2f} MB; "
-            f"max|dO| {e['max_abs_diff']:.2e}; HBM bytes {e['hbm_bytes_per_call']}")
+        parts = [f"{p} {e[p]['ms']['median']:.4f} ms, {e[p]['peak_extra_bytes'] / 1e6:.2f} MB"
+                 for p in IO_PATHS if p in e]
+        log(f"[io] n={n}: " + "; ".join(parts) + f"; HBM bytes {e['hbm_bytes_per_call']}")
     last = entries[-1]
     result = {
         "metric": "forward time, materialising / fused (one head, bf16, d=128)",
-        "value": round(last["materialising"]["ms"]["median"] / last["fused"]["ms"]["median"], 3),
+        "value": (round(last["materialising"]["ms"]["median"] / last["fused"]["ms"]["median"], 3)
+                  if "materialising" in last and "fused" in last else None),
         "unit": "x", "n_gpus": 1, "steps": args.io_calls, "warmup": 2,
         "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), bf16)",
@@ -614,7 +645,7 @@ def time_per_step(fn, steps, warmup):
 class Problem:
     """Device buffers of one workload and its fwd / fwd+bwd step functions."""
 
-    def __init__(self, w, cpu_inputs=None):
+    def __init__(self, w, cpu_inputs=None, split=True):
         import torch
         import exact_tiled_attention_29_amd as fa
         import workloads
@@ -628,12 +659,18 @@ class Problem:
         dt = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
         need = fa.fa_bwd_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.d, dt, fa._mask_code(w.causal))
         self.ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+        # the forward's key-split workspace (grids with few query tiles)
+        need_f = fa.fa_fwd_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.d, dt,
+                                           fa._mask_code(w.causal)) if split else 0
+        self.split = split
+        self.fws = torch.empty(need_f, dtype=torch.uint8, device=dev) if need_f else None
         self.fa = fa
 
     def fwd(self, ev=None):
         if ev is not None:
             ev[0].record()
-        self.fa.forward(self.q, self.k, self.v, self.w.causal, out=self.o, lse=self.lse)
+        self.fa.forward(self.q, self.k, self.v, self.w.causal, out=self.o, lse=self.lse,
+                        split=self.split, workspace=self.fws)
         if ev is not None:
             ev[1].record()
 
@@ -643,12 +680,12 @@ class Problem:
                          workspace=self.ws, grads=self.grads, events=evb)
 
 
-def config_entry(name, steps=30, warmup=5):
+def config_entry(name, steps=30, warmup=5, split=True):
     """Forward-only and fwd+bwd times of a named workload (median and min of
     `steps` event-timed steps) with the metric's FLOP convention."""
     import workloads
     w = workloads.WORKLOADS[name]
-    pr = Problem(w)
+    pr = Problem(w, split=split)
     f = _stats(time_per_step(pr.fwd, steps, warmup))
     a = _stats(time_per_step(pr.step, steps, warmup))
     fl_f, fl_a = w.fwd_flop(), w.fwd_bwd_flop()
@@ -691,10 +728,14 @@ def main():
     ap.add_argument("--summary-out", default=PMC_SUMMARY)
     ap.add_argument("--summary-copy-mib", type=int, default=512)
     ap.add_argument("--summary-command", default="", help="command line recorded in a summary")
+    ap.add_argument("--no-split", action="store_true",
+                    help="never split the forward's keys over workgroups (fa_fwd instead of fa_fwd_ws)")
     ap.add_argument("--io", action="store_true",
                     help="fused vs materialising forward, one head, d = 128 (page 1, section 4)")
     ap.add_argument("--io-n", type=int, default=0, help="one size for --io (default: all)")
     ap.add_argument("--io-calls", type=int, default=10, help="timed calls per path for --io")
+    ap.add_argument("--io-path", default="all", choices=("all",) + IO_PATHS,
+                    help="one forward only (for a profiler run of that path)")
     ap.add_argument("--summarize-io", metavar="DIR",
                     help="write the IO summary from DIR/fN (FETCH_SIZE) and DIR/wN (WRITE_SIZE)")
     ap.add_argument("--rows", action="store_true",
@@ -758,7 +799,7 @@ def main():
 
     log(f"[bench] workload {w.name}: B={w.batch} H={w.heads} n_q={w.n_q} n_k={w.n_k} d={w.d} "
         f"{w.dtype} causal={w.causal}")
-    pr = Problem(w)
+    pr = Problem(w, split=not args.no_split)
 
     if args.copy_mib:
         a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -881,7 +922,7 @@ def main():
         configs = {}
         for name in ("tiny_f32", "tiny_f32_causal", "self_b4h16_n1024_d64",
                      "long_b1h8_n32768_d128_causal", "cross_b8h12_q1000_k3000_d64"):
-            configs[name], cfg_probs[name] = config_entry(name)
+            configs[name], cfg_probs[name] = config_entry(name, split=not args.no_split)
         result["configs"] = configs
 
     # Socket power and clock while the headline step runs back to back: the

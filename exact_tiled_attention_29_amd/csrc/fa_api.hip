@@ -59,6 +59,17 @@ size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
     return 2 * align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * sizeof(float));
 }
 
+// Key split of the bf16 dQ kernel for these sizes (none for float32).
+fa::DqSplit dq_plan(long long bh, int n_q, int n_k, int d, int dtype) {
+    return dtype == FA_BF16 ? fa::dq_split_plan(bh, n_q, n_k, d) : fa::DqSplit{1, n_k};
+}
+
+// The backward's workspace with the partials of a key-split dQ after the
+// row arrays.
+size_t workspace_bytes_split(long long bh, int n_q, int d, int dtype, const fa::DqSplit& sp) {
+    return workspace_bytes(bh, n_q, d, dtype) + align_up(fa::dq_part_bytes(sp, bh, n_q, d));
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
 
 // Device address of `scratch` on the current device, looked up once per
@@ -162,7 +173,8 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int
     if (check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, 1.0f, &empty) != FA_OK)
         return SIZE_MAX;
     if (empty) return 0;
-    return workspace_bytes((long long)batch * heads, n_q, d, dtype);
+    const long long bh = (long long)batch * heads;
+    return workspace_bytes_split(bh, n_q, d, dtype, dq_plan(bh, n_q, n_k, d, dtype));
 }
 
 }  // extern "C"
@@ -172,12 +184,13 @@ namespace {
 // The backward's host checks and launch, shared by fa_bwd_timed and
 // fa_bwd_noalloc. get_ws(need, &ws) supplies the workspace once every
 // argument has been checked (returns a status); it is not called for an
-// empty call.
-template <typename GetWs>
+// empty call. fits(bytes) says whether a workspace of that size (with the
+// dQ split's partials) is available; if not, dQ runs without the split.
+template <typename GetWs, typename Fits>
 int bwd_checked(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                 const float* lse, const void* d_o, void* dq, void* dk, void* dv,
                 int batch, int heads, int n_q, int n_k, int d, int dtype, int causal, float scale,
-                void* stream, void* const* events, GetWs&& get_ws) {
+                void* stream, void* const* events, GetWs&& get_ws, Fits&& fits) {
     bool empty = false;
     int st = check_common(batch, heads, n_q, n_k, d, dtype, o_dtype, causal, scale, &empty);
     if (st != FA_OK) return st;
@@ -193,8 +206,10 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, int 
         return hip_status(e);
     }
     if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return FA_E_NULLPTR;
+    fa::DqSplit sp = dq_plan(bh, n_q, n_k, d, dtype);
+    if (!fits(workspace_bytes_split(bh, n_q, d, dtype, sp))) sp = fa::DqSplit{1, n_k};
     void* workspace = nullptr;
-    st = get_ws(workspace_bytes(bh, n_q, d, dtype), &workspace);
+    st = get_ws(workspace_bytes_split(bh, n_q, d, dtype, sp), &workspace);
     if (st != FA_OK) return st;
     fa::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.d_o = d_o;
@@ -208,6 +223,9 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, int 
     a.l2pad = dtype == FA_BF16
                   ? (float*)(w + align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * sizeof(float)))
                   : nullptr;
+    a.dq_nsplit = sp.nsplit;
+    a.dq_kchunk = sp.kchunk;
+    a.dq_part = sp.nsplit > 1 ? (float*)(w + workspace_bytes(bh, n_q, d, dtype)) : nullptr;
     return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
 
@@ -226,7 +244,7 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, int
         if (((uintptr_t)workspace) % kAlign != 0) return (int)FA_E_WORKSPACE;
         *ws = workspace;
         return (int)FA_OK;
-    });
+    }, [](size_t) { return true; });
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
@@ -249,7 +267,7 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, i
         if (need > FA_BWD_NOALLOC_SCRATCH_BYTES) return (int)FA_E_SCRATCH;
         *ws = scratch_on_current_device();
         return *ws ? (int)FA_OK : (int)FA_E_HIP;
-    });
+    }, [](size_t need) { return need <= FA_BWD_NOALLOC_SCRATCH_BYTES; });
 }
 
 int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float scale, float* lse,

@@ -564,12 +564,16 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
 // --------------------------------------------------------------------------
 // 3. dQ: query-stationary.
 // --------------------------------------------------------------------------
+// Key split (nsplit > 1, grids with few query tiles): virtual head
+// bhv = bh * nsplit + s sums dS K over keys [s * kchunk, (s + 1) * kchunk)
+// only and writes that fp32 partial of dQ at bhv in `part`; dq_reduce_kernel
+// adds the partials (dQ is linear in the keys' terms).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
-    bf16* __restrict__ dQ, int n_q, int n_k, int coff, int n_q_pad, int n_qtiles, float scale,
-    float scale2) {
+    bf16* __restrict__ dQ, float* __restrict__ part, int n_q, int n_k_all, int coff, int n_q_pad,
+    int n_qtiles, float scale, float scale2, int nsplit, int kchunk) {
     constexpr int RW = 32;               // query rows per wave
     constexpr int BR = 4 * RW;           // query rows per workgroup
     constexpr int KK = D / 16;
@@ -586,16 +590,22 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
 
-    int bh, rank;   // rank 0 = last query tile: longest causal work first
-    work_item(blockIdx.x, gridDim.x / n_qtiles, n_qtiles, &bh, &rank);
+    int bhv, rank;   // rank 0 = last query tile: longest causal work first
+    work_item(blockIdx.x, gridDim.x / n_qtiles, n_qtiles, &bhv, &rank);
     const int qt = n_qtiles - 1 - rank;
     const int q0 = qt * BR;
     const int qw = q0 + wave * RW;
+    // this workgroup's keys: [k_lo, k_lo + n_k) of head bh, with the causal
+    // diagonal moved to those local key indices
+    const int bh = bhv / nsplit;
+    const int k_lo = (bhv - bh * nsplit) * kchunk;
+    const int n_k = max(0, min(n_k_all, k_lo + kchunk) - k_lo);
+    coff -= k_lo;
 
     const bf16* Qh = Q + (size_t)bh * n_q * D;
     const bf16* dOh = dO + (size_t)bh * n_q * D;
-    const bf16* Kh = K + (size_t)bh * n_k * D;
-    const bf16* Vh = V + (size_t)bh * n_k * D;
+    const bf16* Kh = K + ((size_t)bh * n_k_all + k_lo) * D;
+    const bf16* Vh = V + ((size_t)bh * n_k_all + k_lo) * D;
 
     // Q and dO rows as B operands (column = query, k = d); L2 and D of the
     // lane's query (both halves of the lane pair hold the same row).
@@ -755,17 +765,50 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     }
 
     if (row < n_q) {
-        const size_t obase = ((size_t)bh * n_q + row) * D;
+        if (part) {
+            float* pb = part + ((size_t)bhv * n_q + row) * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bf16x4 pk;
+                for (int i = 0; i < 4; ++i)
+                    *(float4*)(pb + 32 * db + 8 * i + 4 * g) =
+                        make_float4(acc[db][4 * i] * scale, acc[db][4 * i + 1] * scale,
+                                    acc[db][4 * i + 2] * scale, acc[db][4 * i + 3] * scale);
+        } else {
+            const size_t obase = ((size_t)bh * n_q + row) * D;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pk[j] = to_bf16(acc[db][4 * i + j] * scale);
-                *(bf16x4*)(dQ + obase + 32 * db + 8 * i + 4 * g) = pk;
-            }
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16x4 pk;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pk[j] = to_bf16(acc[db][4 * i + j] * scale);
+                    *(bf16x4*)(dQ + obase + 32 * db + 8 * i + 4 * g) = pk;
+                }
+        }
     }
+}
+
+// dQ = the sum of the key-split partials in split order (deterministic),
+// rounded once to bf16; one thread per 4 columns of a row.
+template <int D>
+__global__ __launch_bounds__(kThreads) void dq_reduce_kernel(const float* __restrict__ part,
+                                                             bf16* __restrict__ dQ, long long rows,
+                                                             int n_q, int nsplit) {
+    const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= rows * (D / 4)) return;
+    const long long row = i / (D / 4);
+    const int c = (int)(i - row * (D / 4)) * 4;
+    const long long bh = row / n_q;
+    const size_t first = ((size_t)bh * nsplit * n_q + (size_t)(row - bh * n_q)) * D + c;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s = 0; s < nsplit; ++s) {
+        const float4 x = *(const float4*)(part + first + (size_t)s * n_q * D);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    bf16x4 pk;
+    pk[0] = to_bf16(acc.x); pk[1] = to_bf16(acc.y); pk[2] = to_bf16(acc.z); pk[3] = to_bf16(acc.w);
+    *(bf16x4*)(dQ + (size_t)row * D + c) = pk;
 }
 
 template <int D, bool CAUSAL>
@@ -777,8 +820,11 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     constexpr int NP = dkdv_pairs<D>();
     const int n_ktiles = (a.n_k + 32 * NP - 1) / (32 * NP);
     const int n_qtiles = (a.n_q + 127) / 128;
+    const int nsplit = a.dq_part ? a.dq_nsplit : 1;
+    const long long rows = (long long)a.bh * a.n_q;
     if (nb > 0x7fffffffLL || (long long)a.bh * n_ktiles > 0x7fffffffLL ||
-        (long long)a.bh * n_qtiles > 0x7fffffffLL)
+        (long long)a.bh * nsplit * n_qtiles > 0x7fffffffLL ||
+        (rows * (D / 4) + kThreads - 1) / kThreads > 0x7fffffffLL)
         return hipErrorInvalidValue;
     hipError_t e = record_stage(a, 0, st);
     if (e != hipSuccess) return e;
@@ -800,11 +846,17 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 2, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * n_qtiles)), dim3(kThreads), 0,
-                       st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o,
-                       (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dq,
-                       a.n_q, a.n_k, a.coff, n_q_pad, n_qtiles, a.scale, a.scale * kLog2e);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.bh * nsplit * n_qtiles)),
+                       dim3(kThreads), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                       (const bf16*)a.d_o, (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dq,
+                       nsplit > 1 ? a.dq_part : nullptr, a.n_q, a.n_k, a.coff, n_q_pad, n_qtiles,
+                       a.scale, a.scale * kLog2e, nsplit, nsplit > 1 ? a.dq_kchunk : a.n_k);
     e = hipGetLastError();
+    if (e == hipSuccess && nsplit > 1) {
+        hipLaunchKernelGGL((dq_reduce_kernel<D>), dim3((unsigned)((rows * (D / 4) + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, st, (const float*)a.dq_part, (bf16*)a.dq, rows, a.n_q, nsplit);
+        e = hipGetLastError();
+    }
     return e == hipSuccess ? record_stage(a, 3, st) : e;
 }
 
@@ -823,6 +875,37 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
     if (nb > 65536) nb = 65536;
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)nb), dim3(kThreads), 0, st, (unsigned*)p, n);
     return hipGetLastError();
+}
+
+// Key split of the dQ kernel for grids with few query tiles: when its
+// 128-row workgroups would fill at most half of the resident slots (two per
+// CU, one at d = 256) and there are at least 2048 keys, split each tile's
+// keys into the fewest chunks (whole 64-key tiles, at least 256 keys) whose
+// workgroups fill the slots in whole rounds (or four or more); failing
+// that, into as many as fill one round. nsplit = 1: no split.
+DqSplit dq_split_plan(long long bh, int n_q, int n_k, int d) {
+    DqSplit sp{1, n_k};
+    if (n_k < 2048) return sp;
+    const long long nwg = bh * ((n_q + 127) / 128);
+    const long long slots = (long long)device_cu_count() * (d >= 256 ? 1 : 2);
+    if (slots <= 0 || 2 * nwg > slots) return sp;
+    const int s_max = n_k / 256;
+    auto plan = [&](int s) {
+        const int chunk = ((n_k + s - 1) / s + kBC - 1) / kBC * kBC;
+        return DqSplit{(n_k + chunk - 1) / chunk, chunk};
+    };
+    for (int s = 2; s <= s_max && nwg * s <= 8 * slots; ++s) {
+        const DqSplit p = plan(s);
+        const long long n = nwg * p.nsplit;
+        if (n % slots == 0 || n >= 4 * slots) return p;
+    }
+    const long long s_round = (slots + nwg - 1) / nwg;
+    const int s = (int)(s_round < s_max ? s_round : s_max);
+    return s >= 2 ? plan(s) : sp;
+}
+
+size_t dq_part_bytes(const DqSplit& sp, long long bh, int n_q, int d) {
+    return sp.nsplit > 1 ? (size_t)sp.nsplit * (size_t)bh * (size_t)n_q * (size_t)d * sizeof(float) : 0;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {

@@ -40,7 +40,19 @@ struct BwdArgs {
     float* drow;    // fp32 D = rowsum(dO * O): [bh, n_q] (fp32 path), or -D [bh, n_q_pad] (bf16)
     float* l2pad;   // fp32 [bh, n_q_pad] L * log2(e), +inf on padding rows (bf16 path)
     hipEvent_t const* events;  // NULL or 4 events: before D, before dK/dV, after dK/dV, end
+    float* dq_part;  // NULL, or fp32 [bh * dq_nsplit, n_q, d]: key-split partials of dQ (bf16 path)
+    int dq_nsplit;   // key chunks of the dQ kernel when dq_part is set
+    int dq_kchunk;   // keys per chunk, a multiple of 64
 };
+
+// Key split of the bf16 dQ kernel for grids with few query tiles
+// (fa_bwd.hip); nsplit = 1 means none.
+struct DqSplit {
+    int nsplit;
+    int kchunk;
+};
+DqSplit dq_split_plan(long long bh, int n_q, int n_k, int d);
+size_t dq_part_bytes(const DqSplit& sp, long long bh, int n_q, int d);
 
 // Record stage event i of a backward call (no-op without events).
 inline hipError_t record_stage(const BwdArgs& a, int i, hipStream_t st) {

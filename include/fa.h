@@ -132,8 +132,12 @@ int fa_fwd_ws(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (0 for an empty
  * call). bf16: the fp32 row term -D and L * log2(e), each [B,H,ceil(n_q/32)*32]
- * and 256-byte aligned; float32: D [B,H,n_q]. Returns SIZE_MAX for
- * arguments fa_bwd would reject (so 0 always means an empty call).
+ * and 256-byte aligned, and, for grids with few query tiles (the dQ
+ * kernel's 128-row workgroups would fill at most half of the GPU and there
+ * are at least 2048 keys), the fp32 partials of dQ over key chunks
+ * [chunks, B,H,n_q,d]; float32: D [B,H,n_q]. The answer depends on the
+ * current device's compute-unit count. Returns SIZE_MAX for arguments
+ * fa_bwd would reject (so 0 always means an empty call).
  */
 size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
                               int dtype, int causal);
@@ -157,6 +161,10 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
  * 256-byte aligned, owned by the caller, contents on entry ignored. Calls
  * that overlap in time must not share a workspace.
  * Results are deterministic: the same inputs give bitwise the same outputs.
+ * With few query tiles (see fa_bwd_workspace_bytes) the dQ kernel splits
+ * the keys over several workgroups, each summing dS K over its chunk in
+ * fp32, and a second kernel adds the chunks in a fixed order and rounds dQ
+ * once to bf16.
  * Accuracy (bf16): dS is rounded to bf16 for the dQ and dK products; dQ's
  * error relative to each row's norm was about 2.4e-3 (median) at every
  * context length measured, 32K to 512K keys (causal, d = 128): it does not
@@ -195,11 +203,14 @@ int fa_bwd_timed(const void* q, const void* k, const void* v,
  * same arguments and results as fa_bwd, without the workspace. Its scratch
  * is a static array of FA_BWD_NOALLOC_SCRATCH_BYTES in the library's code
  * object, one per GPU, held from the first call on that GPU until the
- * process ends; the call itself allocates nothing. It serves problems with
- * fa_bwd_workspace_bytes(...) <= FA_BWD_NOALLOC_SCRATCH_BYTES (bf16: about
- * 2 million query rows over all batches and heads) and returns FA_E_SCRATCH
- * beyond that, with nothing launched. Calls on one GPU share that GPU's
- * scratch: calls that overlap in time on the same GPU (other streams,
+ * process ends; the call itself allocates nothing. It serves problems whose
+ * row arrays fit in the scratch (the bf16 -D and L * log2(e), or the float32
+ * D, that fa_bwd_workspace_bytes counts; bf16: about 2 million query rows
+ * over all batches and heads) and returns FA_E_SCRATCH beyond that, with
+ * nothing launched. Where fa_bwd would split dQ's keys and the partials do
+ * not fit in the scratch as well, it runs dQ unsplit (the same dQ up to
+ * rounding); otherwise its results equal fa_bwd's bitwise. Calls on one
+ * GPU share that GPU's scratch: calls that overlap in time on the same GPU (other streams,
  * other host threads) race and give undefined results. The first call on a
  * GPU looks the scratch address up (hipGetSymbolAddress); a failure there
  * returns FA_E_HIP.

@@ -178,35 +178,36 @@ def test_rocminfo_parse(monkeypatch):
                     "name": "AMD Instinct MI355X"}
 
 
-def test_summarize_io_splits_paths_and_scales(tmp_path, monkeypatch):
-    # FETCH_SIZE of the 512 MiB copy reads half its bytes (scale 2), WRITE_SIZE
-    # all of them; 3 calls per path (three fused dispatches)
+def test_summarize_io_per_path_and_scaled(tmp_path, monkeypatch):
+    # one path per process; FETCH_SIZE of the 512 MiB copy reads half its
+    # bytes (scale 2), WRITE_SIZE all of them; three calls per path
     mib = 1 << 20
-    for n in (1024, 4096):
-        fetch = [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "FETCH_SIZE", "Counter_Value": 512 * 1024 / 2},
-                 {"Kernel_Name": "Cijk_Alik_Bljk_BBS", "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0 * n / 1024},
-                 {"Kernel_Name": "Cijk_Alik_Bljk_BBS", "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0 * n / 1024},
-                 {"Kernel_Name": "cunn_SoftMaxForward", "Counter_Name": "FETCH_SIZE", "Counter_Value": 600.0 * n / 1024},
-                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "FETCH_SIZE", "Counter_Value": 10.0},
-                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "FETCH_SIZE", "Counter_Value": 10.0},
-                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "FETCH_SIZE", "Counter_Value": 10.0},
-                 {"Kernel_Name": "at::native::reduce_kernel", "Counter_Name": "FETCH_SIZE", "Counter_Value": 1e6}]
-        write = [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "WRITE_SIZE", "Counter_Value": 512 * 1024},
-                 {"Kernel_Name": "cunn_SoftMaxForward", "Counter_Name": "WRITE_SIZE", "Counter_Value": 300.0 * n / 1024},
-                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0},
-                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0},
-                 {"Kernel_Name": "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0}]
-        _write_csv(str(tmp_path / "io" / f"f{n}" / "run_counter_collection.csv"), fetch)
-        _write_csv(str(tmp_path / "io" / f"w{n}" / "run_counter_collection.csv"), write)
+    copy_f = {"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "FETCH_SIZE", "Counter_Value": 512 * 1024 / 2}
+    copy_w = {"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "WRITE_SIZE", "Counter_Value": 512 * 1024}
+
+    def rows(counter, spec):
+        return [{"Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v} for k, v in spec]
+    gemm, soft = "Cijk_Alik_Bljk_BBS", "cunn_SoftMaxForward"
+    pp, merge = "_ZN2fa12_GLOBAL__N_113fwd_pp_kernelIL", "_ZN2fa12_GLOBAL__N_116fwd_merge_kernelIL"
+    other = "at::native::reduce_kernel"
+    runs = {
+        "materialising": ([copy_f] + rows("FETCH_SIZE", [(gemm, 300.0)] * 6 + [(soft, 600.0)] * 3 + [(other, 1e6)]),
+                          [copy_w] + rows("WRITE_SIZE", [(gemm, 100.0)] * 6 + [(soft, 300.0)] * 3)),
+        "fused": ([copy_f] + rows("FETCH_SIZE", [(pp, 10.0)] * 3), [copy_w] + rows("WRITE_SIZE", [(pp, 5.0)] * 3)),
+        "fused_split": ([copy_f] + rows("FETCH_SIZE", [(pp, 4.0)] * 12 + [(merge, 20.0)] * 3),
+                        [copy_w] + rows("WRITE_SIZE", [(pp, 4.0)] * 12 + [(merge, 5.0)] * 3)),
+    }
+    for path, (f, w) in runs.items():
+        _write_csv(str(tmp_path / "io" / f"f4096_{path}" / "run_counter_collection.csv"), f)
+        _write_csv(str(tmp_path / "io" / f"w4096_{path}" / "run_counter_collection.csv"), w)
     out = tmp_path / "io.txt"
     bench.summarize_io(str(tmp_path / "io"), str(out), "cmd", copy_bytes=512 * mib)
     monkeypatch.setattr(bench, "IO_SUMMARY", str(out))
-    t = bench.io_traffic_from_summary(1024)
-    # materialising: fetch (300 + 300 + 600) KiB x 2 + write 300 KiB, over 3 calls;
-    # fused: (30 x 2 + 15) KiB over 3 calls; the reduce kernel counts for neither
-    assert t["materialising"] == (1200 * 2 + 300) * 1024 / 3
-    assert t["fused"] == (30 * 2 + 15) * 1024 / 3
-    assert bench.io_traffic_from_summary(4096)["materialising"] == (4800 * 2 + 1200) * 1024 / 3
-    assert bench.io_traffic_from_summary(2048) is None
+    t = bench.io_traffic_from_summary(4096)
+    # per call: fetch KiB x 2 + write KiB, over the 3 calls the anchor kernel counts
+    assert t["materialising"] == ((6 * 300 + 3 * 600) * 2 + 6 * 100 + 3 * 300) * 1024 / 3
+    assert t["fused"] == (3 * 10 * 2 + 3 * 5) * 1024 / 3
+    assert t["fused_split"] == ((12 * 4 + 3 * 20) * 2 + 12 * 4 + 3 * 5) * 1024 / 3
+    assert bench.io_traffic_from_summary(1024) == {}
     out.write_text(out.read_text().replace(bench.kernel_source_hash(), "0000000000000000"))
-    assert bench.io_traffic_from_summary(1024) is None
+    assert bench.io_traffic_from_summary(4096) == {}

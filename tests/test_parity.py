@@ -257,10 +257,14 @@ SPLIT_SHAPES = [
 
 
 @pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", SPLIT_SHAPES)
-def test_split_forward(B, H, n_q, n_k, d, dtype, causal):
+def test_split_shapes(B, H, n_q, n_k, d, dtype, causal):
+    # the forward and the backward's dQ kernel both split the keys here
     mask = {False: 0, True: 1, "bottom_right": 2}[causal]
     need = fa.fa_fwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask)
     assert need > 0, "this shape should take the key split"
+    base = 2 * ((B * H * ((n_q + 31) // 32 * 32) * 4 + 255) // 256 * 256)
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask) > base, \
+        "the backward should hold dQ partials"
     w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
     q, k, v, do = make_inputs(w, seed=n_q + 3 * n_k)
     res = run(q, k, v, do, causal)            # forward() splits when asked to
@@ -279,6 +283,13 @@ def test_split_forward(B, H, n_q, n_k, d, dtype, causal):
     assert torch.equal(live, torch.isfinite(l2))
     assert float((o1 - o2).abs().max()) <= 1e-2
     assert float((l1[live] - l2[live]).abs().max()) <= 1e-3
+    # the split backward is deterministic too
+    og, lg = fa.forward(qg, kg, vg, causal)
+    dog = do.cuda()
+    g1 = fa.backward(qg, kg, vg, og, lg, dog, causal)
+    g2 = fa.backward(qg, kg, vg, og, lg, dog, causal)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
 
 
 def test_split_forward_needs_its_workspace():

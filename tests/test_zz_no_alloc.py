@@ -52,6 +52,24 @@ def test_noalloc_matches_workspace_path(first, second):
             assert torch.equal(a, b), f"{w}: {name} differs from fa_bwd"
 
 
+def test_noalloc_with_the_dq_key_split():
+    # few query tiles and 4096 keys: fa_bwd splits dQ's keys. Small partials
+    # fit in the scratch and noalloc splits the same way (bitwise equal);
+    # 33 MB of partials do not, and noalloc runs dQ unsplit (dK, dV bitwise
+    # equal, dQ the same up to rounding).
+    small = workloads.custom(1, 2, 128, 4096, 64, "bf16", "bottom_right")
+    ref, got = _grads_both_ways(small)
+    for name, a, b in zip(("dQ", "dK", "dV"), ref, got):
+        assert torch.equal(a, b), f"{small}: {name} differs from fa_bwd"
+    big = workloads.custom(1, 2, 4096, 4096, 128, "bf16", True)
+    need = fa.fa_bwd_workspace_bytes(1, 2, 4096, 4096, 128, fa.FA_BF16, 1)
+    assert need > fa.FA_BWD_NOALLOC_SCRATCH_BYTES
+    ref, got = _grads_both_ways(big)
+    assert torch.equal(ref[1], got[1]) and torch.equal(ref[2], got[2])
+    dq_err = float((ref[0].float() - got[0].float()).abs().max() / ref[0].float().abs().max())
+    assert dq_err <= 1e-2
+
+
 def test_noalloc_refuses_beyond_scratch():
     # needs 2 * 64 * 32800 * 4 bytes > 16 MiB of scratch: refused, nothing launched
     q = torch.zeros(1, 64, 32800, 64, dtype=torch.bfloat16, device="cuda")
