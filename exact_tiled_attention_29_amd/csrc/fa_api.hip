@@ -59,15 +59,24 @@ size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
     return 2 * align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * sizeof(float));
 }
 
-// Key split of the bf16 dQ kernel for these sizes (none for float32).
-fa::DqSplit dq_plan(long long bh, int n_q, int n_k, int d, int dtype) {
-    return dtype == FA_BF16 ? fa::dq_split_plan(bh, n_q, n_k, d) : fa::DqSplit{1, n_k};
+// Splits of the bf16 backward for these sizes (none for float32): keys of
+// the dQ kernel, queries of the dK/dV kernel.
+struct BwdPlan {
+    fa::DqSplit dq, kv;
+};
+BwdPlan bwd_plan(long long bh, int n_q, int n_k, int d, int dtype) {
+    if (dtype != FA_BF16) return {{1, n_k}, {1, n_q}};
+    return {fa::dq_split_plan(bh, n_q, n_k, d), fa::kv_split_plan(bh, n_q, n_k, d)};
 }
 
-// The backward's workspace with the partials of a key-split dQ after the
-// row arrays.
-size_t workspace_bytes_split(long long bh, int n_q, int d, int dtype, const fa::DqSplit& sp) {
-    return workspace_bytes(bh, n_q, d, dtype) + align_up(fa::dq_part_bytes(sp, bh, n_q, d));
+// The backward's workspace: the row arrays, then the dQ partials, then the
+// dK and dV partials (each 256-byte aligned).
+size_t dq_part_offset(long long bh, int n_q, int d, int dtype) { return workspace_bytes(bh, n_q, d, dtype); }
+size_t kv_part_offset(long long bh, int n_q, int d, int dtype, const BwdPlan& p) {
+    return dq_part_offset(bh, n_q, d, dtype) + align_up(fa::dq_part_bytes(p.dq, bh, n_q, d));
+}
+size_t workspace_bytes_split(long long bh, int n_q, int n_k, int d, int dtype, const BwdPlan& p) {
+    return kv_part_offset(bh, n_q, d, dtype, p) + align_up(fa::kv_part_bytes(p.kv, bh, n_k, d));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
@@ -174,7 +183,7 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d, int
         return SIZE_MAX;
     if (empty) return 0;
     const long long bh = (long long)batch * heads;
-    return workspace_bytes_split(bh, n_q, d, dtype, dq_plan(bh, n_q, n_k, d, dtype));
+    return workspace_bytes_split(bh, n_q, n_k, d, dtype, bwd_plan(bh, n_q, n_k, d, dtype));
 }
 
 }  // extern "C"
@@ -206,10 +215,11 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, int 
         return hip_status(e);
     }
     if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return FA_E_NULLPTR;
-    fa::DqSplit sp = dq_plan(bh, n_q, n_k, d, dtype);
-    if (!fits(workspace_bytes_split(bh, n_q, d, dtype, sp))) sp = fa::DqSplit{1, n_k};
+    BwdPlan plan = bwd_plan(bh, n_q, n_k, d, dtype);
+    if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.kv = fa::DqSplit{1, n_q};
+    if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.dq = fa::DqSplit{1, n_k};
     void* workspace = nullptr;
-    st = get_ws(workspace_bytes_split(bh, n_q, d, dtype, sp), &workspace);
+    st = get_ws(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan), &workspace);
     if (st != FA_OK) return st;
     fa::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.d_o = d_o;
@@ -223,9 +233,12 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, int 
     a.l2pad = dtype == FA_BF16
                   ? (float*)(w + align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * sizeof(float)))
                   : nullptr;
-    a.dq_nsplit = sp.nsplit;
-    a.dq_kchunk = sp.kchunk;
-    a.dq_part = sp.nsplit > 1 ? (float*)(w + workspace_bytes(bh, n_q, d, dtype)) : nullptr;
+    a.dq_nsplit = plan.dq.nsplit;
+    a.dq_kchunk = plan.dq.kchunk;
+    a.dq_part = plan.dq.nsplit > 1 ? (float*)(w + dq_part_offset(bh, n_q, d, dtype)) : nullptr;
+    a.kv_nsplit = plan.kv.nsplit;
+    a.kv_qchunk = plan.kv.kchunk;
+    a.kv_part = plan.kv.nsplit > 1 ? (float*)(w + kv_part_offset(bh, n_q, d, dtype, plan)) : nullptr;
     return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
 

@@ -121,12 +121,18 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 template <int D>
 constexpr int dkdv_pairs() { return D >= 256 ? 2 : 4; }
 
+// Query split (nsplit > 1, grids with few key blocks): virtual head
+// bhv = bh * nsplit + s takes query rows [s * qchunk, (s + 1) * qchunk) only
+// (qchunk a multiple of 32) and writes its fp32 partials of dK and dV at bhv
+// in part_k / part_v; split_reduce_kernel adds them (both are sums over the
+// queries).
 template <int D, bool CAUSAL, int NP>
 __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ l2p, const float* __restrict__ dp,
-    bf16* __restrict__ dK, bf16* __restrict__ dV,
-    int n_q, int n_k, int coff, int n_q_pad, int n_ktiles, float scale, float scale2) {
+    bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ part_k,
+    float* __restrict__ part_v, int n_q_all, int n_k, int coff, int n_q_pad, int n_ktiles,
+    float scale, float scale2, int nsplit, int qchunk) {
     constexpr int NW = 2 * NP;         // waves
     constexpr int BKV = 32 * NP;       // keys per workgroup
     constexpr int KK = D / 16;
@@ -159,16 +165,22 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     const bool role_a = wave < NP;
     const int pair = wave & (NP - 1);
 
-    int bh, kt;   // rank = key tile, ascending: longest causal work first
-    work_item(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, &bh, &kt);
+    int bhv, kt;   // rank = key tile, ascending: longest causal work first
+    work_item(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, &bhv, &kt);
     const int k0 = kt * BKV;
     const int kw0 = k0 + 32 * pair;      // the pair's first key
     const int key = kw0 + r;             // this lane's key (column of S, dP)
+    // this workgroup's queries: rows [q_lo, q_lo + n_q) of head bh, with the
+    // causal diagonal moved to those local row indices
+    const int bh = bhv / nsplit;
+    const int q_lo = (bhv - bh * nsplit) * qchunk;
+    const int n_q = max(0, min(n_q_all, q_lo + qchunk) - q_lo);
+    coff += q_lo;
 
-    const bf16* Qh = Q + (size_t)bh * n_q * D;
-    const bf16* dOh = dO + (size_t)bh * n_q * D;
-    const float* l2h = l2p + (size_t)bh * n_q_pad;
-    const float* dph = dp + (size_t)bh * n_q_pad;
+    const bf16* Qh = Q + ((size_t)bh * n_q_all + q_lo) * D;
+    const bf16* dOh = dO + ((size_t)bh * n_q_all + q_lo) * D;
+    const float* l2h = l2p + (size_t)bh * n_q_pad + q_lo;
+    const float* dph = dp + (size_t)bh * n_q_pad + q_lo;
 
     // K (wave A) or V (wave B) rows of the pair's keys as B operands
     // (column = key, k = d).
@@ -194,8 +206,8 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     // chunks) is issued by wave b % NW.
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, n_q * D * 2);
     const __amdgpu_buffer_rsrc_t dors = make_rsrc(dOh, n_q * D * 2);
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(l2h, n_q_pad * 4);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dph, n_q_pad * 4);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(l2h, (n_q_pad - q_lo) * 4);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dph, (n_q_pad - q_lo) * 4);
     auto issue_tile = [&](bf16* Sd, int t) {
         const int q0 = t * kBQ;
 #pragma unroll
@@ -549,16 +561,28 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
     }
 
     // Epilogue: wave A stores dV, wave B stores dK = scale * acc; rows =
-    // keys kw0 + acc_row(v, g), column = d.
-    bf16* out = role_a ? dV : dK;
+    // keys kw0 + acc_row(v, g), column = d. Under the query split: the fp32
+    // partials of virtual head bhv.
     const float f = role_a ? 1.0f : scale;
+    if (part_k) {
+        float* out = role_a ? part_v : part_k;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int kr = kw0 + acc_row(v, g);
-            if (kr < n_k) out[((size_t)bh * n_k + kr) * D + 32 * db + r] = to_bf16(acc[db][v] * f);
-        }
+            for (int v = 0; v < 16; ++v) {
+                const int kr = kw0 + acc_row(v, g);
+                if (kr < n_k) out[((size_t)bhv * n_k + kr) * D + 32 * db + r] = acc[db][v] * f;
+            }
+    } else {
+        bf16* out = role_a ? dV : dK;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int kr = kw0 + acc_row(v, g);
+                if (kr < n_k) out[((size_t)bh * n_k + kr) * D + 32 * db + r] = to_bf16(acc[db][v] * f);
+            }
+    }
 }
 
 // --------------------------------------------------------------------------
@@ -789,26 +813,38 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     }
 }
 
-// dQ = the sum of the key-split partials in split order (deterministic),
-// rounded once to bf16; one thread per 4 columns of a row.
+// A gradient as the sum of its split partials ([bh, nsplit, n, D] fp32), in
+// split order (deterministic), rounded once to bf16 into [bh, n, D]; one
+// thread per 4 columns of a row. Used for dQ (key split) and dK, dV (query
+// split).
 template <int D>
-__global__ __launch_bounds__(kThreads) void dq_reduce_kernel(const float* __restrict__ part,
-                                                             bf16* __restrict__ dQ, long long rows,
-                                                             int n_q, int nsplit) {
+__global__ __launch_bounds__(kThreads) void split_reduce_kernel(const float* __restrict__ part,
+                                                                bf16* __restrict__ out, long long rows,
+                                                                int n, int nsplit) {
     const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
     if (i >= rows * (D / 4)) return;
     const long long row = i / (D / 4);
     const int c = (int)(i - row * (D / 4)) * 4;
-    const long long bh = row / n_q;
-    const size_t first = ((size_t)bh * nsplit * n_q + (size_t)(row - bh * n_q)) * D + c;
+    const long long bh = row / n;
+    const size_t first = ((size_t)bh * nsplit * n + (size_t)(row - bh * n)) * D + c;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int s = 0; s < nsplit; ++s) {
-        const float4 x = *(const float4*)(part + first + (size_t)s * n_q * D);
+        const float4 x = *(const float4*)(part + first + (size_t)s * n * D);
         acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
     }
     bf16x4 pk;
     pk[0] = to_bf16(acc.x); pk[1] = to_bf16(acc.y); pk[2] = to_bf16(acc.z); pk[3] = to_bf16(acc.w);
-    *(bf16x4*)(dQ + (size_t)row * D + c) = pk;
+    *(bf16x4*)(out + (size_t)row * D + c) = pk;
+}
+
+template <int D>
+hipError_t launch_split_reduce(const float* part, void* out, long long rows, int n, int nsplit,
+                               hipStream_t st) {
+    const long long nb = (rows * (D / 4) + kThreads - 1) / kThreads;
+    if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((split_reduce_kernel<D>), dim3((unsigned)nb), dim3(kThreads), 0, st, part,
+                       (bf16*)out, rows, n, nsplit);
+    return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
@@ -821,10 +857,9 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     const int n_ktiles = (a.n_k + 32 * NP - 1) / (32 * NP);
     const int n_qtiles = (a.n_q + 127) / 128;
     const int nsplit = a.dq_part ? a.dq_nsplit : 1;
-    const long long rows = (long long)a.bh * a.n_q;
-    if (nb > 0x7fffffffLL || (long long)a.bh * n_ktiles > 0x7fffffffLL ||
-        (long long)a.bh * nsplit * n_qtiles > 0x7fffffffLL ||
-        (rows * (D / 4) + kThreads - 1) / kThreads > 0x7fffffffLL)
+    const int kv_split = a.kv_part ? a.kv_nsplit : 1;
+    if (nb > 0x7fffffffLL || (long long)a.bh * kv_split * n_ktiles > 0x7fffffffLL ||
+        (long long)a.bh * nsplit * n_qtiles > 0x7fffffffLL)
         return hipErrorInvalidValue;
     hipError_t e = record_stage(a, 0, st);
     if (e != hipSuccess) return e;
@@ -839,11 +874,19 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 1, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NP>), dim3((unsigned)(a.bh * n_ktiles)), dim3(128 * NP), 0,
-                       st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o,
-                       (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dk, (bf16*)a.dv,
-                       a.n_q, a.n_k, a.coff, n_q_pad, n_ktiles, a.scale, a.scale * kLog2e);
+    float* part_k = kv_split > 1 ? a.kv_part : nullptr;
+    float* part_v = kv_split > 1 ? a.kv_part + (size_t)kv_split * a.bh * a.n_k * D : nullptr;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NP>), dim3((unsigned)((long long)a.bh * kv_split * n_ktiles)),
+                       dim3(128 * NP), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                       (const bf16*)a.d_o, (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dk,
+                       (bf16*)a.dv, part_k, part_v, a.n_q, a.n_k, a.coff, n_q_pad, n_ktiles, a.scale,
+                       a.scale * kLog2e, kv_split, kv_split > 1 ? a.kv_qchunk : a.n_q);
     e = hipGetLastError();
+    if (e == hipSuccess && kv_split > 1) {
+        const long long krows = (long long)a.bh * a.n_k;
+        e = launch_split_reduce<D>(part_k, a.dk, krows, a.n_k, kv_split, st);
+        if (e == hipSuccess) e = launch_split_reduce<D>(part_v, a.dv, krows, a.n_k, kv_split, st);
+    }
     if (e == hipSuccess) e = record_stage(a, 2, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.bh * nsplit * n_qtiles)),
@@ -852,11 +895,8 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
                        nsplit > 1 ? a.dq_part : nullptr, a.n_q, a.n_k, a.coff, n_q_pad, n_qtiles,
                        a.scale, a.scale * kLog2e, nsplit, nsplit > 1 ? a.dq_kchunk : a.n_k);
     e = hipGetLastError();
-    if (e == hipSuccess && nsplit > 1) {
-        hipLaunchKernelGGL((dq_reduce_kernel<D>), dim3((unsigned)((rows * (D / 4) + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, st, (const float*)a.dq_part, (bf16*)a.dq, rows, a.n_q, nsplit);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess && nsplit > 1)
+        e = launch_split_reduce<D>(a.dq_part, a.dq, (long long)a.bh * a.n_q, a.n_q, nsplit, st);
     return e == hipSuccess ? record_stage(a, 3, st) : e;
 }
 
@@ -906,6 +946,37 @@ DqSplit dq_split_plan(long long bh, int n_q, int n_k, int d) {
 
 size_t dq_part_bytes(const DqSplit& sp, long long bh, int n_q, int d) {
     return sp.nsplit > 1 ? (size_t)sp.nsplit * (size_t)bh * (size_t)n_q * (size_t)d * sizeof(float) : 0;
+}
+
+// Query split of the dK/dV kernel for grids with few key blocks: when its
+// workgroups (one per CU) would fill at most half of the CUs and there are
+// at least 2048 queries, split the queries into the fewest chunks (multiples
+// of 256 rows) whose workgroups fill the CUs in whole rounds (or four or
+// more); failing that, into as many as fill one round. nsplit = 1: none.
+DqSplit kv_split_plan(long long bh, int n_q, int n_k, int d) {
+    DqSplit sp{1, n_q};
+    if (n_q < 2048) return sp;
+    const int bkv = 32 * (d >= 256 ? 2 : 4);
+    const long long nwg = bh * ((n_k + bkv - 1) / bkv);
+    const long long slots = device_cu_count();
+    if (slots <= 0 || 2 * nwg > slots) return sp;
+    const int s_max = n_q / 256;
+    auto plan = [&](int s) {
+        const int chunk = ((n_q + s - 1) / s + 255) / 256 * 256;
+        return DqSplit{(n_q + chunk - 1) / chunk, chunk};
+    };
+    for (int s = 2; s <= s_max && nwg * s <= 8 * slots; ++s) {
+        const DqSplit p = plan(s);
+        const long long n = nwg * p.nsplit;
+        if (n % slots == 0 || n >= 4 * slots) return p;
+    }
+    const long long s_round = (slots + nwg - 1) / nwg;
+    const int s = (int)(s_round < s_max ? s_round : s_max);
+    return s >= 2 ? plan(s) : sp;
+}
+
+size_t kv_part_bytes(const DqSplit& sp, long long bh, int n_k, int d) {
+    return sp.nsplit > 1 ? 2 * (size_t)sp.nsplit * (size_t)bh * (size_t)n_k * (size_t)d * sizeof(float) : 0;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {

@@ -43,6 +43,9 @@ struct BwdArgs {
     float* dq_part;  // NULL, or fp32 [bh * dq_nsplit, n_q, d]: key-split partials of dQ (bf16 path)
     int dq_nsplit;   // key chunks of the dQ kernel when dq_part is set
     int dq_kchunk;   // keys per chunk, a multiple of 64
+    float* kv_part;  // NULL, or fp32 partials of dK then dV, each [bh * kv_nsplit, n_k, d] (bf16 path)
+    int kv_nsplit;   // query chunks of the dK/dV kernel when kv_part is set
+    int kv_qchunk;   // queries per chunk, a multiple of 256
 };
 
 // Key split of the bf16 dQ kernel for grids with few query tiles
@@ -53,6 +56,10 @@ struct DqSplit {
 };
 DqSplit dq_split_plan(long long bh, int n_q, int n_k, int d);
 size_t dq_part_bytes(const DqSplit& sp, long long bh, int n_q, int d);
+// Query split of the bf16 dK/dV kernel for grids with few key blocks
+// (nsplit chunks of kchunk = a multiple of 256 queries); nsplit = 1: none.
+DqSplit kv_split_plan(long long bh, int n_q, int n_k, int d);
+size_t kv_part_bytes(const DqSplit& sp, long long bh, int n_k, int d);
 
 // Record stage event i of a backward call (no-op without events).
 inline hipError_t record_stage(const BwdArgs& a, int i, hipStream_t st) {

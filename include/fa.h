@@ -135,7 +135,9 @@ int fa_fwd_ws(const void* q, const void* k, const void* v,
  * and 256-byte aligned, and, for grids with few query tiles (the dQ
  * kernel's 128-row workgroups would fill at most half of the GPU and there
  * are at least 2048 keys), the fp32 partials of dQ over key chunks
- * [chunks, B,H,n_q,d]; float32: D [B,H,n_q]. The answer depends on the
+ * [chunks, B,H,n_q,d], and for grids with few key blocks (at least 2048
+ * queries) those of dK and dV over query chunks [2, chunks, B,H,n_k,d];
+ * float32: D [B,H,n_q]. The answer depends on the
  * current device's compute-unit count. Returns SIZE_MAX for arguments
  * fa_bwd would reject (so 0 always means an empty call).
  */
@@ -164,7 +166,8 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int n_q, int n_k, int d,
  * With few query tiles (see fa_bwd_workspace_bytes) the dQ kernel splits
  * the keys over several workgroups, each summing dS K over its chunk in
  * fp32, and a second kernel adds the chunks in a fixed order and rounds dQ
- * once to bf16.
+ * once to bf16; with few key blocks the dK/dV kernel splits the queries
+ * the same way.
  * Accuracy (bf16): dS is rounded to bf16 for the dQ and dK products; dQ's
  * error relative to each row's norm was about 2.4e-3 (median) at every
  * context length measured, 32K to 512K keys (causal, d = 128): it does not
@@ -207,9 +210,9 @@ int fa_bwd_timed(const void* q, const void* k, const void* v,
  * row arrays fit in the scratch (the bf16 -D and L * log2(e), or the float32
  * D, that fa_bwd_workspace_bytes counts; bf16: about 2 million query rows
  * over all batches and heads) and returns FA_E_SCRATCH beyond that, with
- * nothing launched. Where fa_bwd would split dQ's keys and the partials do
- * not fit in the scratch as well, it runs dQ unsplit (the same dQ up to
- * rounding); otherwise its results equal fa_bwd's bitwise. Calls on one
+ * nothing launched. Where fa_bwd would split a kernel and the partials do
+ * not fit in the scratch as well, it runs that kernel unsplit (the same
+ * gradients up to rounding); otherwise its results equal fa_bwd's bitwise. Calls on one
  * GPU share that GPU's scratch: calls that overlap in time on the same GPU (other streams,
  * other host threads) race and give undefined results. The first call on a
  * GPU looks the scratch address up (hipGetSymbolAddress); a failure there

@@ -292,6 +292,57 @@ def test_split_shapes(B, H, n_q, n_k, d, dtype, causal):
         assert torch.equal(a, b)
 
 
+# Few key blocks against many queries: the dK/dV kernel splits its queries
+# (fp32 partials of dK and dV, then a sum); the forward and dQ do not split.
+KV_SPLIT_SHAPES = [
+    (1, 2, 2300, 300, 128, "bf16", False),
+    (1, 1, 4000, 1000, 64, "bf16", True),
+    (1, 2, 2500, 500, 32, "bf16", "bottom_right"),
+    (1, 1, 2200, 200, 256, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", KV_SPLIT_SHAPES)
+def test_kv_split_shapes(B, H, n_q, n_k, d, dtype, causal):
+    mask = {False: 0, True: 1, "bottom_right": 2}[causal]
+    base = 2 * ((B * H * ((n_q + 31) // 32 * 32) * 4 + 255) // 256 * 256)
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask) > base
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
+    q, k, v, do = make_inputs(w, seed=n_q + 7 * n_k + d)
+    res = run(q, k, v, do, causal)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    check_heads(res, q, k, v, do, causal, dtype, heads, tag="kv split " + str((B, H, n_q, n_k, d, causal)))
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    og, lg = fa.forward(qg, kg, vg, causal)
+    g1 = fa.backward(qg, kg, vg, og, lg, dog, causal)
+    g2 = fa.backward(qg, kg, vg, og, lg, dog, causal)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+# The dQ key split also serves the head dims without a forward split (32,
+# 96, 256; d = 256 has one dQ workgroup per CU).
+DQ_SPLIT_DIMS = [
+    (1, 2, 200, 4096, 32, "bf16", False),
+    (1, 2, 300, 2500, 96, "bf16", True),
+    (1, 1, 256, 3000, 256, "bf16", "bottom_right"),
+    (1, 2, 2100, 2048, 256, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", DQ_SPLIT_DIMS)
+def test_dq_split_head_dims(B, H, n_q, n_k, d, dtype, causal):
+    mask = {False: 0, True: 1, "bottom_right": 2}[causal]
+    assert fa.fa_fwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask) == 0
+    base = 2 * ((B * H * ((n_q + 31) // 32 * 32) * 4 + 255) // 256 * 256)
+    assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask) > base
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
+    q, k, v, do = make_inputs(w, seed=n_q + 5 * n_k + d)
+    res = run(q, k, v, do, causal)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    check_heads(res, q, k, v, do, causal, dtype, heads, tag="dq split " + str((B, H, n_q, n_k, d, causal)))
+
+
 def test_split_forward_needs_its_workspace():
     B, H, n_q, n_k, d = 1, 1, 4096, 4096, 128
     need = fa.fa_fwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, 0)

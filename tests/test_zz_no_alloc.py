@@ -55,8 +55,8 @@ def test_noalloc_matches_workspace_path(first, second):
 def test_noalloc_with_the_dq_key_split():
     # few query tiles and 4096 keys: fa_bwd splits dQ's keys. Small partials
     # fit in the scratch and noalloc splits the same way (bitwise equal);
-    # 33 MB of partials do not, and noalloc runs dQ unsplit (dK, dV bitwise
-    # equal, dQ the same up to rounding).
+    # 33 MB of partials (dQ's, and dK/dV's from the query split) do not, and
+    # noalloc runs both kernels unsplit (the same gradients up to rounding).
     small = workloads.custom(1, 2, 128, 4096, 64, "bf16", "bottom_right")
     ref, got = _grads_both_ways(small)
     for name, a, b in zip(("dQ", "dK", "dV"), ref, got):
@@ -65,9 +65,9 @@ def test_noalloc_with_the_dq_key_split():
     need = fa.fa_bwd_workspace_bytes(1, 2, 4096, 4096, 128, fa.FA_BF16, 1)
     assert need > fa.FA_BWD_NOALLOC_SCRATCH_BYTES
     ref, got = _grads_both_ways(big)
-    assert torch.equal(ref[1], got[1]) and torch.equal(ref[2], got[2])
-    dq_err = float((ref[0].float() - got[0].float()).abs().max() / ref[0].float().abs().max())
-    assert dq_err <= 1e-2
+    for name, a, b in zip(("dQ", "dK", "dV"), ref, got):
+        err = float((a.float() - b.float()).abs().max() / a.float().abs().max())
+        assert err <= 1e-2, f"{name}: {err}"
 
 
 def test_noalloc_refuses_beyond_scratch():
