@@ -218,7 +218,8 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
             const int chunk = is_q ? b : b - NCH;
             const int p = 64 * chunk + lane;
             const int row = p / (D / 8), pc = p % (D / 8);
-            const int boff = ((q0 + row) * D + 8 * (pc ^ tile_swz<D>(row))) * 2;
+            // unsigned: (n_q rounded up to the tile) * D * 2 may pass 2^31 - 1
+            const unsigned boff = ((unsigned)(q0 + row) * D + 8u * (unsigned)(pc ^ tile_swz<D>(row))) * 2u;
             if (is_q) load_lds16(qrs, boff, q_of(Sd) + 512 * chunk);
             else load_lds16(dors, boff, do_of(Sd) + 512 * chunk);
         }
@@ -667,7 +668,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
             const int p = 64 * b + lane;
             const int rw = p / (D / 8), pc = p % (D / 8);
             const int chunk = pc ^ tile_swz<D>(rw);
-            const int boff = ((ks + rw) * D + 8 * chunk) * 2;
+            const unsigned boff = ((unsigned)(ks + rw) * D + 8u * (unsigned)chunk) * 2u;   // see above
             load_lds16(krs, boff, Kd + 512 * b);
             load_lds16(vrs, boff, Vd + 512 * b);
         }

@@ -189,9 +189,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // lds): lane l's 16 bytes, read at byte offset `voff` of the resource, land at
 // lds_base + 16*l; lds_base must be wave-uniform. A buffer (not a flat/global)
 // load, so the compiler keeps precise waits on the LDS reads that follow.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, int voff, void* lds_base) {
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, unsigned voff, void* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds_base),
-                                             16, voff, 0, 0, 0);
+                                             16, (int)voff, 0, 0, 0);
 }
 
 // Work order of a grid of n_bh * n_tiles workgroups (one per (head, tile)).

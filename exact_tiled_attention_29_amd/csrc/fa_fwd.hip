@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
             const int p = 64 * b + lane;
             const int row = p / (D / 8), pc = p % (D / 8);
             const int chunk = pc ^ tile_swz<D>(row);
-            const int boff = ((ks + row) * D + 8 * chunk) * 2;
+            // unsigned: (n_k rounded up to the tile) * D * 2 may pass 2^31 - 1
+            const unsigned boff = ((unsigned)(ks + row) * D + 8u * (unsigned)chunk) * 2u;
             load_lds16(krs, boff, Kd + 512 * b);
             load_lds16(vrs, boff, Vd + 512 * b);
         }

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
         const int p = 64 * b + lane;
         const int row = p / (D / 8), pc = p % (D / 8);
         const unsigned boff = ((unsigned)(ks + row) * D + 8u * (unsigned)(pc ^ tile_swz<D>(row))) * 2u;
-        load_lds16(rs, (int)(valid ? boff : 0x80000000u), dst + 512 * b);
+        load_lds16(rs, valid ? boff : 0x80000000u, dst + 512 * b);
     };
     // The same copy during the loop, where this wave always copies chunks
     // 4c + sub: the lane's part of the offset is computed once (cpart[c]),
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
     }
     auto copy_share = [&](__amdgpu_buffer_rsrc_t rs, bf16* dst, int ks, int c, bool valid) __attribute__((always_inline)) {
         const unsigned base = valid ? (unsigned)ks * D * 2u : 0x80000000u;
-        load_lds16(rs, (int)(base + cpart[c]), dst + 512 * (4 * c + sub));
+        load_lds16(rs, base + cpart[c], dst + 512 * (4 * c + sub));
     };
     // One tensor tile copied by all eight waves.
     auto copy_by_all = [&](__amdgpu_buffer_rsrc_t rs, bf16* dst, int ks) __attribute__((always_inline)) {
