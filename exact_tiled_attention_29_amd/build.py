@@ -52,10 +52,12 @@ def sources():
 
 
 # Kernels whose registers must never spill to scratch (a spill in the hot
-# loop puts memory waits between the MFMAs). The float32 kernels keep a
-# whole row per thread and are allowed to spill at large head dims.
+# loop puts memory waits between the MFMAs or FMAs): every attention and row
+# kernel (the float32 ones spread a row over up to four lanes so that at
+# most 32 columns of each row vector sit in a thread's registers).
 NO_SPILL = ("fwd_bf16_kernel", "fwd_pp_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
-            "bwd_pre_kernel", "row_softmax_kernel")
+            "bwd_pre_kernel", "row_softmax_kernel", "fwd_merge_kernel", "split_reduce_kernel",
+            "fwd_f32_kernel", "bwd_dkdv_f32_kernel", "bwd_dq_f32_kernel", "bwd_pre_f32_kernel")
 _REMARK = re.compile(r"remark:\s+(Function Name|VGPRs Spill|ScratchSize \[bytes/lane\]|VGPRs|AGPRs|"
                      r"Occupancy \[waves/SIMD\]):\s+(\S+)")
 

@@ -3,9 +3,11 @@
 // Same algorithm as the bf16 path: the tiled online-softmax forward of page 1
 // ("05_flash_attention.py", section 2) and its recomputation backward
 // (section 3), with the derivative rules of page 3 ("Flash Attention"),
-// section 1.5. Each thread owns one query row (forward, dQ) or one key row
-// (dK, dV) and keeps it in registers; key/query tiles of 32 rows are staged
-// in LDS and read as broadcasts. The backward's dQ comes from its own pass
+// section 1.5. A group of G adjacent lanes owns one query row (forward, dQ)
+// or one key row (dK, dV), each lane holding C = D / G of its columns in
+// registers (at most 32: d = 128 is four lanes of 32), and the row's dot
+// products are summed over the group with quad permutes; key/query tiles of
+// 32 rows are staged in LDS and read as broadcasts. The backward's dQ comes from its own pass
 // over the key tiles, so no atomics are needed and results are deterministic.
 // The causal diagonal is a runtime offset coff (key j visible to query i iff
 // j <= i + coff); a row that sees no key gets O = 0, L = -inf and zero dQ,
@@ -17,13 +19,35 @@ namespace fa {
 
 namespace {
 
-constexpr int kRows = 64;   // rows (threads) per workgroup
+constexpr int kRows = 64;   // rows per workgroup
 constexpr int kTile = 32;   // rows per staged tile
+
+// A row's d values are spread over G adjacent lanes of C columns each
+// (lanes 4i .. 4i + 3 hold one, two or four whole rows, so the quad permutes
+// below stay inside a row): d = 16 one lane; 32 two lanes of 16; 64, 96,
+// 128 four lanes of 16, 24, 32. A thread keeps at most 32 columns of each
+// of its row vectors in registers, and a 64-row workgroup has 2-4 waves.
+template <int D>
+struct Split {
+    static constexpr int G = D <= 16 ? 1 : (D == 32 ? 2 : 4);
+    static constexpr int C = D / G;
+    static constexpr int kThreads = kRows * G;
+};
+
+// Sum over the G lanes of a row (DPP quad permutes: lane ^ 1, lane ^ 2).
+template <int G>
+__device__ __forceinline__ float row_sum(float x) {
+    if (G >= 2)
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+    if (G >= 4)
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+    return x;
+}
 
 template <int D>
 __device__ __forceinline__ void stage_rows(float* dst, const float* src, int row0, int n, int tid) {
     // kTile x D floats, rows past n are zero.
-    for (int i = tid; i < kTile * D / 4; i += kRows) {
+    for (int i = tid; i < kTile * D / 4; i += Split<D>::kThreads) {
         const int row = i / (D / 4), c = i % (D / 4);
         const int gr = row0 + row;
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -33,24 +57,26 @@ __device__ __forceinline__ void stage_rows(float* dst, const float* src, int row
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void fwd_f32_kernel(
+__global__ __launch_bounds__(Split<D>::kThreads) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ Lse, int n_q, int n_k, int coff, int n_qtiles,
     float scale2) {
+    constexpr int G = Split<D>::G, C = Split<D>::C;
     __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
     const int tid = threadIdx.x;
+    const int col0 = (tid % G) * C;     // this lane's columns
     const int bh = blockIdx.x / n_qtiles;
     const int q0 = (blockIdx.x % n_qtiles) * kRows;
-    const int row = q0 + tid;
+    const int row = q0 + tid / G;
     const float* Kh = K + (size_t)bh * n_k * D;
     const float* Vh = V + (size_t)bh * n_k * D;
 
-    float q[D], o[D];
+    float q[C], o[C];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        q[d] = row < n_q ? Q[((size_t)bh * n_q + row) * D + d] * scale2 : 0.0f;
-        o[d] = 0.0f;
+    for (int c = 0; c < C; ++c) {
+        q[c] = row < n_q ? Q[((size_t)bh * n_q + row) * D + col0 + c] * scale2 : 0.0f;
+        o[c] = 0.0f;
     }
     float m = kNegInf, l = 0.0f;
     int kend = n_k;
@@ -66,7 +92,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
         for (int j = 0; j < kTile; ++j) {
             float acc = 0.0f;
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc = fmaf(q[d], Ks[j * D + d], acc);
+            for (int c = 0; c < C; ++c) acc = fmaf(q[c], Ks[j * D + col0 + c], acc);
+            acc = row_sum<G>(acc);
             const int key = ks + j;
             if (key >= n_k || (CAUSAL && key > row + coff)) acc = kNegInf;
             s[j] = acc;
@@ -77,21 +104,21 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
         const float corr = fast_exp2(m - m_use);
         l *= corr;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] *= corr;
+        for (int c = 0; c < C; ++c) o[c] *= corr;
 #pragma unroll
         for (int j = 0; j < kTile; ++j) {
             const float p = fast_exp2(s[j] - m_use);
             l += p;
 #pragma unroll
-            for (int d = 0; d < D; ++d) o[d] = fmaf(p, Vs[j * D + d], o[d]);
+            for (int c = 0; c < C; ++c) o[c] = fmaf(p, Vs[j * D + col0 + c], o[c]);
         }
         m = m_new;
     }
     if (row < n_q) {
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;   // no visible key: O = 0, L = -inf
 #pragma unroll
-        for (int d = 0; d < D; ++d) O[((size_t)bh * n_q + row) * D + d] = o[d] * inv;
-        Lse[(size_t)bh * n_q + row] = kLn2 * (m + fast_log2(l));
+        for (int c = 0; c < C; ++c) O[((size_t)bh * n_q + row) * D + col0 + c] = o[c] * inv;
+        if (col0 == 0) Lse[(size_t)bh * n_q + row] = kLn2 * (m + fast_log2(l));
     }
 }
 
@@ -112,29 +139,33 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(
     drow[row] = acc;
 }
 
-// dK, dV: one key row per thread, query tiles staged in LDS.
+// dK, dV: one key row per G lanes, query tiles staged in LDS. Lanes of a
+// key past n_k compute with zero K, V rows and store nothing (no branch
+// around the row sums).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
+__global__ __launch_bounds__(Split<D>::kThreads) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ drow,
     float* __restrict__ dK, float* __restrict__ dV, int n_q, int n_k, int coff, int n_ktiles,
     float scale, float scale2) {
+    constexpr int G = Split<D>::G, C = Split<D>::C;
     __shared__ __attribute__((aligned(16))) float Qs[kTile * D];
     __shared__ __attribute__((aligned(16))) float dOs[kTile * D];
     __shared__ float Ls[kTile], Ds[kTile];
     const int tid = threadIdx.x;
+    const int col0 = (tid % G) * C;
     const int bh = blockIdx.x / n_ktiles;
     const int k0 = (blockIdx.x % n_ktiles) * kRows;
-    const int key = k0 + tid;
+    const int key = k0 + tid / G;
     const float* Qh = Q + (size_t)bh * n_q * D;
     const float* dOh = dO + (size_t)bh * n_q * D;
 
-    float kr[D], vr[D], dk[D], dv[D];
+    float kr[C], vr[C], dk[C], dv[C];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        kr[d] = key < n_k ? K[((size_t)bh * n_k + key) * D + d] * scale2 : 0.0f;
-        vr[d] = key < n_k ? V[((size_t)bh * n_k + key) * D + d] : 0.0f;
-        dk[d] = dv[d] = 0.0f;
+    for (int c = 0; c < C; ++c) {
+        kr[c] = key < n_k ? K[((size_t)bh * n_k + key) * D + col0 + c] * scale2 : 0.0f;
+        vr[c] = key < n_k ? V[((size_t)bh * n_k + key) * D + col0 + c] : 0.0f;
+        dk[c] = dv[c] = 0.0f;
     }
     const int qbeg = CAUSAL ? (max(0, k0 - coff) / kTile) * kTile : 0;  // rows >= k0 - coff
     for (int qs = qbeg; qs < n_q; qs += kTile) {
@@ -148,56 +179,59 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
             Ds[tid] = q < n_q ? drow[(size_t)bh * n_q + q] : 0.0f;
         }
         __syncthreads();
-        if (key >= n_k) continue;
 #pragma unroll 4
         for (int i = 0; i < kTile; ++i) {
             const int q = qs + i;
             float s = 0.0f, dp = 0.0f;
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                s = fmaf(Qs[i * D + d], kr[d], s);
-                dp = fmaf(dOs[i * D + d], vr[d], dp);
+            for (int c = 0; c < C; ++c) {
+                s = fmaf(Qs[i * D + col0 + c], kr[c], s);
+                dp = fmaf(dOs[i * D + col0 + c], vr[c], dp);
             }
+            s = row_sum<G>(s);
+            dp = row_sum<G>(dp);
             float p = fast_exp2(s - Ls[i]);
-            if (q >= n_q || (CAUSAL && key > q + coff)) p = 0.0f;
+            if (key >= n_k || q >= n_q || (CAUSAL && key > q + coff)) p = 0.0f;
             const float ds = p * (dp - Ds[i]);
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                dv[d] = fmaf(p, dOs[i * D + d], dv[d]);
-                dk[d] = fmaf(ds, Qs[i * D + d], dk[d]);
+            for (int c = 0; c < C; ++c) {
+                dv[c] = fmaf(p, dOs[i * D + col0 + c], dv[c]);
+                dk[c] = fmaf(ds, Qs[i * D + col0 + c], dk[c]);
             }
         }
     }
     if (key < n_k) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            dK[((size_t)bh * n_k + key) * D + d] = dk[d] * scale;
-            dV[((size_t)bh * n_k + key) * D + d] = dv[d];
+        for (int c = 0; c < C; ++c) {
+            dK[((size_t)bh * n_k + key) * D + col0 + c] = dk[c] * scale;
+            dV[((size_t)bh * n_k + key) * D + col0 + c] = dv[c];
         }
     }
 }
 
-// dQ: one query row per thread, key tiles staged in LDS.
+// dQ: one query row per G lanes, key tiles staged in LDS.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
+__global__ __launch_bounds__(Split<D>::kThreads) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ drow,
     float* __restrict__ dQ, int n_q, int n_k, int coff, int n_qtiles, float scale, float scale2) {
+    constexpr int G = Split<D>::G, C = Split<D>::C;
     __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
     const int tid = threadIdx.x;
+    const int col0 = (tid % G) * C;
     const int bh = blockIdx.x / n_qtiles;
     const int q0 = (blockIdx.x % n_qtiles) * kRows;
-    const int row = q0 + tid;
+    const int row = q0 + tid / G;
     const float* Kh = K + (size_t)bh * n_k * D;
     const float* Vh = V + (size_t)bh * n_k * D;
 
-    float q[D], dor[D], dq[D];
+    float q[C], dor[C], dq[C];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        q[d] = row < n_q ? Q[((size_t)bh * n_q + row) * D + d] * scale2 : 0.0f;
-        dor[d] = row < n_q ? dO[((size_t)bh * n_q + row) * D + d] : 0.0f;
-        dq[d] = 0.0f;
+    for (int c = 0; c < C; ++c) {
+        q[c] = row < n_q ? Q[((size_t)bh * n_q + row) * D + col0 + c] * scale2 : 0.0f;
+        dor[c] = row < n_q ? dO[((size_t)bh * n_q + row) * D + col0 + c] : 0.0f;
+        dq[c] = 0.0f;
     }
     const float lse = row < n_q ? Lse[(size_t)bh * n_q + row] : kNegInf;
     const float l2 = lse > kNegInf ? lse * kLog2e : __builtin_huge_valf();   // P = 0 if no key
@@ -209,27 +243,28 @@ __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
         stage_rows<D>(Ks, Kh, ks, n_k, tid);
         stage_rows<D>(Vs, Vh, ks, n_k, tid);
         __syncthreads();
-        if (row >= n_q) continue;
 #pragma unroll 4
         for (int j = 0; j < kTile; ++j) {
             const int key = ks + j;
             float s = 0.0f, dp = 0.0f;
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                s = fmaf(q[d], Ks[j * D + d], s);
-                dp = fmaf(dor[d], Vs[j * D + d], dp);
+            for (int c = 0; c < C; ++c) {
+                s = fmaf(q[c], Ks[j * D + col0 + c], s);
+                dp = fmaf(dor[c], Vs[j * D + col0 + c], dp);
             }
+            s = row_sum<G>(s);
+            dp = row_sum<G>(dp);
             float p = fast_exp2(s - l2);
             if (key >= n_k || (CAUSAL && key > row + coff)) p = 0.0f;
             const float ds = p * (dp - Dr);
 #pragma unroll
-            for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, Ks[j * D + d], dq[d]);
+            for (int c = 0; c < C; ++c) dq[c] = fmaf(ds, Ks[j * D + col0 + c], dq[c]);
         }
     }
     if (row < n_q) {
         // Ks holds K * 1 (unscaled); q was pre-scaled, so dq needs the scale.
 #pragma unroll
-        for (int d = 0; d < D; ++d) dQ[((size_t)bh * n_q + row) * D + d] = dq[d] * scale;
+        for (int c = 0; c < C; ++c) dQ[((size_t)bh * n_q + row) * D + col0 + c] = dq[c] * scale;
     }
 }
 
@@ -238,7 +273,7 @@ hipError_t fwd_launch(const FwdArgs& a, hipStream_t st) {
     const int nt = (a.n_q + kRows - 1) / kRows;
     const long long nwg = (long long)a.bh * nt;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kRows), 0, st,
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(Split<D>::kThreads), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                        a.n_q, a.n_k, a.coff, nt, a.scale * kLog2e);
     return hipGetLastError();
@@ -259,14 +294,14 @@ hipError_t bwd_launch(const BwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 1, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkt)), dim3(kRows), 0, st,
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkt)), dim3(Split<D>::kThreads), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.d_o,
                        a.lse, a.drow, (float*)a.dk, (float*)a.dv, a.n_q, a.n_k, a.coff, nkt, a.scale,
                        a.scale * kLog2e);
     e = hipGetLastError();
     if (e == hipSuccess) e = record_stage(a, 2, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqt)), dim3(kRows), 0, st,
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqt)), dim3(Split<D>::kThreads), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.d_o,
                        a.lse, a.drow, (float*)a.dq, a.n_q, a.n_k, a.coff, nqt, a.scale, a.scale * kLog2e);
     e = hipGetLastError();

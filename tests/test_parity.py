@@ -228,6 +228,10 @@ EDGE_DIMS = [
     (1, 2, 517, 200, 256, "bf16", "bottom_right"),
     (1, 2, 140, 70, 96, "f32", True),
     (1, 1, 100, 100, 96, "f32", "bottom_right"),
+    # float32 rows over two and four lanes, several tiles and workgroups
+    (2, 2, 300, 517, 128, "f32", True),
+    (1, 3, 333, 129, 96, "f32", False),
+    (1, 2, 257, 300, 64, "f32", "bottom_right"),
 ]
 
 
