@@ -83,3 +83,45 @@ def test_noalloc_refuses_beyond_scratch():
     assert st == 9 and fa.fa_status_str(st).startswith("problem needs more")
     torch.cuda.synchronize()
     assert bool((dq == 7.0).all())
+
+
+def test_noalloc_under_graph_capture():
+    # The callers fa_bwd_noalloc is for: a forward (fa_fwd, no workspace) and
+    # the no-alloc backward captured in one HIP graph, replayed three times
+    # with eager work and synchronisations between the replays; every replay
+    # must give the eager results bit for bit.
+    w = workloads.custom(2, 4, 300, 300, 128, "bf16", True)
+    q, k, v, do = (t.cuda() for t in workloads.make_inputs(w, seed=5))
+    dt, mask, scale = fa.FA_BF16, fa._mask_code(w.causal), 1.0 / w.d ** 0.5
+    o = torch.empty_like(q)
+    lse = torch.empty(w.batch, w.heads, w.n_q, device="cuda")
+    grads = tuple(torch.empty_like(t) for t in (q, k, v))
+
+    def step(stream):
+        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dt, lse.data_ptr(),
+                       w.batch, w.heads, w.n_q, w.n_k, w.d, dt, mask, scale, stream)
+        assert st == 0
+        st = fa.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dt, lse.data_ptr(),
+                               do.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                               w.batch, w.heads, w.n_q, w.n_k, w.d, dt, mask, scale, stream)
+        assert st == 0
+
+    step(torch.cuda.current_stream().cuda_stream)      # eager (also looks the scratch up)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, lse) + grads]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step(s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (o, lse) + grads:
+            t.fill_(float("nan"))                         # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("O", "L", "dQ", "dK", "dV"), ref, (o, lse) + grads):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
