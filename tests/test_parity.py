@@ -605,3 +605,32 @@ def test_side_stream():
     torch.cuda.synchronize()
     for a, b in zip(ref, out):
         assert torch.equal(a, b)
+
+
+def _sweep_shapes(count=24, seed=20251):
+    # Seeded random shapes across every path choice: head dims, masks, n_q
+    # above and below n_k, ragged tails, grids that take the key and query
+    # splits and grids that do not.
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(count):
+        d = int(rng.choice([32, 64, 96, 128, 256]))
+        causal = [False, True, "bottom_right"][int(rng.integers(0, 3))]
+        if i % 3 == 0:        # long keys or queries on a small grid: splits
+            n_q, n_k = (int(rng.integers(1, 400)), int(rng.integers(2048, 6000))) if i % 2 == 0 else \
+                       (int(rng.integers(2048, 5000)), int(rng.integers(1, 600)))
+            B, H = 1, int(rng.integers(1, 3))
+        else:
+            n_q, n_k = int(rng.integers(1, 1200)), int(rng.integers(1, 1200))
+            B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        shapes.append((B, H, n_q, n_k, d, "bf16", causal))
+    return shapes
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", _sweep_shapes())
+def test_random_shapes(B, H, n_q, n_k, d, dtype, causal):
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
+    q, k, v, do = make_inputs(w, seed=B * 1000003 + H * 10007 + n_q * 101 + n_k + d)
+    res = run(q, k, v, do, causal)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    check_heads(res, q, k, v, do, causal, dtype, heads, tag="sweep " + str((B, H, n_q, n_k, d, causal)))
