@@ -62,7 +62,7 @@ size_t workspace_bytes(long long bh, int n_q, int d, int dtype) {
 // Splits of the bf16 backward for these sizes (none for float32): keys of
 // the dQ kernel, queries of the dK/dV kernel.
 struct BwdPlan {
-    fa::DqSplit dq, kv;
+    fa::Split dq, kv;
 };
 BwdPlan bwd_plan(long long bh, int n_q, int n_k, int d, int dtype) {
     if (dtype != FA_BF16) return {{1, n_k}, {1, n_q}};
@@ -169,7 +169,7 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, int o_dtype,
     a.o_f32 = o_dtype == FA_F32; a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
     if (dtype != FA_BF16) return hip_status(fa::launch_fwd_f32(a, s));
-    const fa::FwdSplit sp = fa::fwd_split_plan(a);
+    const fa::Split sp = fa::fwd_split_plan(a);
     const size_t need = fa::fwd_split_workspace_bytes(a, sp);
     if (need == 0) return hip_status(fa::launch_fwd_bf16(a, s));
     if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
@@ -216,8 +216,8 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, int 
     }
     if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return FA_E_NULLPTR;
     BwdPlan plan = bwd_plan(bh, n_q, n_k, d, dtype);
-    if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.kv = fa::DqSplit{1, n_q};
-    if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.dq = fa::DqSplit{1, n_k};
+    if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.kv = fa::Split{1, n_q};
+    if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.dq = fa::Split{1, n_k};
     void* workspace = nullptr;
     st = get_ws(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan), &workspace);
     if (st != FA_OK) return st;
@@ -234,10 +234,10 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, int 
                   ? (float*)(w + align_up((size_t)bh * (size_t)fa::dq_rows_padded(n_q) * sizeof(float)))
                   : nullptr;
     a.dq_nsplit = plan.dq.nsplit;
-    a.dq_kchunk = plan.dq.kchunk;
+    a.dq_chunk = plan.dq.chunk;
     a.dq_part = plan.dq.nsplit > 1 ? (float*)(w + dq_part_offset(bh, n_q, d, dtype)) : nullptr;
     a.kv_nsplit = plan.kv.nsplit;
-    a.kv_qchunk = plan.kv.kchunk;
+    a.kv_chunk = plan.kv.chunk;
     a.kv_part = plan.kv.nsplit > 1 ? (float*)(w + kv_part_offset(bh, n_q, d, dtype, plan)) : nullptr;
     return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }

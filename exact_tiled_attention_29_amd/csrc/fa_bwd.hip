@@ -881,7 +881,7 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
                        dim3(128 * NP), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.d_o, (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dk,
                        (bf16*)a.dv, part_k, part_v, a.n_q, a.n_k, a.coff, n_q_pad, n_ktiles, a.scale,
-                       a.scale * kLog2e, kv_split, kv_split > 1 ? a.kv_qchunk : a.n_q);
+                       a.scale * kLog2e, kv_split, kv_split > 1 ? a.kv_chunk : a.n_q);
     e = hipGetLastError();
     if (e == hipSuccess && kv_split > 1) {
         const long long krows = (long long)a.bh * a.n_k;
@@ -894,7 +894,7 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t st) {
                        dim3(kThreads), 0, st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.d_o, (const float*)a.l2pad, (const float*)a.drow, (bf16*)a.dq,
                        nsplit > 1 ? a.dq_part : nullptr, a.n_q, a.n_k, a.coff, n_q_pad, n_qtiles,
-                       a.scale, a.scale * kLog2e, nsplit, nsplit > 1 ? a.dq_kchunk : a.n_k);
+                       a.scale, a.scale * kLog2e, nsplit, nsplit > 1 ? a.dq_chunk : a.n_k);
     e = hipGetLastError();
     if (e == hipSuccess && nsplit > 1)
         e = launch_split_reduce<D>(a.dq_part, a.dq, (long long)a.bh * a.n_q, a.n_q, nsplit, st);
@@ -918,65 +918,25 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Key split of the dQ kernel for grids with few query tiles: when its
-// 128-row workgroups would fill at most half of the resident slots (two per
-// CU, one at d = 256) and there are at least 2048 keys, split each tile's
-// keys into the fewest chunks (whole 64-key tiles, at least 256 keys) whose
-// workgroups fill the slots in whole rounds (or four or more); failing
-// that, into as many as fill one round. nsplit = 1: no split.
-DqSplit dq_split_plan(long long bh, int n_q, int n_k, int d) {
-    DqSplit sp{1, n_k};
-    if (n_k < 2048) return sp;
-    const long long nwg = bh * ((n_q + 127) / 128);
+// Key split of the dQ kernel (128-row workgroups, two resident per CU, one
+// at d = 256; chunks of whole 64-key tiles) and query split of the dK/dV
+// kernel (one workgroup per CU; chunks of 256-row multiples), by the shared
+// rule of plan_split.
+Split dq_split_plan(long long bh, int n_q, int n_k, int d) {
     const long long slots = (long long)device_cu_count() * (d >= 256 ? 1 : 2);
-    if (slots <= 0 || 2 * nwg > slots) return sp;
-    const int s_max = n_k / 256;
-    auto plan = [&](int s) {
-        const int chunk = ((n_k + s - 1) / s + kBC - 1) / kBC * kBC;
-        return DqSplit{(n_k + chunk - 1) / chunk, chunk};
-    };
-    for (int s = 2; s <= s_max && nwg * s <= 8 * slots; ++s) {
-        const DqSplit p = plan(s);
-        const long long n = nwg * p.nsplit;
-        if (n % slots == 0 || n >= 4 * slots) return p;
-    }
-    const long long s_round = (slots + nwg - 1) / nwg;
-    const int s = (int)(s_round < s_max ? s_round : s_max);
-    return s >= 2 ? plan(s) : sp;
+    return plan_split(bh * ((n_q + 127) / 128), slots, n_k, kBC);
 }
 
-size_t dq_part_bytes(const DqSplit& sp, long long bh, int n_q, int d) {
+size_t dq_part_bytes(const Split& sp, long long bh, int n_q, int d) {
     return sp.nsplit > 1 ? (size_t)sp.nsplit * (size_t)bh * (size_t)n_q * (size_t)d * sizeof(float) : 0;
 }
 
-// Query split of the dK/dV kernel for grids with few key blocks: when its
-// workgroups (one per CU) would fill at most half of the CUs and there are
-// at least 2048 queries, split the queries into the fewest chunks (multiples
-// of 256 rows) whose workgroups fill the CUs in whole rounds (or four or
-// more); failing that, into as many as fill one round. nsplit = 1: none.
-DqSplit kv_split_plan(long long bh, int n_q, int n_k, int d) {
-    DqSplit sp{1, n_q};
-    if (n_q < 2048) return sp;
+Split kv_split_plan(long long bh, int n_q, int n_k, int d) {
     const int bkv = 32 * (d >= 256 ? 2 : 4);
-    const long long nwg = bh * ((n_k + bkv - 1) / bkv);
-    const long long slots = device_cu_count();
-    if (slots <= 0 || 2 * nwg > slots) return sp;
-    const int s_max = n_q / 256;
-    auto plan = [&](int s) {
-        const int chunk = ((n_q + s - 1) / s + 255) / 256 * 256;
-        return DqSplit{(n_q + chunk - 1) / chunk, chunk};
-    };
-    for (int s = 2; s <= s_max && nwg * s <= 8 * slots; ++s) {
-        const DqSplit p = plan(s);
-        const long long n = nwg * p.nsplit;
-        if (n % slots == 0 || n >= 4 * slots) return p;
-    }
-    const long long s_round = (slots + nwg - 1) / nwg;
-    const int s = (int)(s_round < s_max ? s_round : s_max);
-    return s >= 2 ? plan(s) : sp;
+    return plan_split(bh * ((n_k + bkv - 1) / bkv), device_cu_count(), n_q, 256);
 }
 
-size_t kv_part_bytes(const DqSplit& sp, long long bh, int n_k, int d) {
+size_t kv_part_bytes(const Split& sp, long long bh, int n_k, int d) {
     return sp.nsplit > 1 ? 2 * (size_t)sp.nsplit * (size_t)bh * (size_t)n_k * (size_t)d * sizeof(float) : 0;
 }
 

@@ -548,7 +548,7 @@ hipError_t launch_pp(const FwdArgs& a, hipStream_t st) {
 // Key-split forward: partials of every split into the workspace (fp32 O,
 // then L, then the bf16-weight logsumexp), then the merge into O and L.
 template <int D, bool CAUSAL, bool OF32>
-hipError_t launch_pp_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st) {
+hipError_t launch_pp_split(const FwdArgs& a, const Split& sp, float* ws, hipStream_t st) {
     const int n_qtiles = (a.n_q + kPPRows - 1) / kPPRows;
     const long long nwg = (long long)a.bh * sp.nsplit * n_qtiles;
     const long long rows = (long long)a.bh * a.n_q;
@@ -558,7 +558,7 @@ hipError_t launch_pp_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipS
     float* plb = pl + (size_t)sp.nsplit * rows;
     hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, true>), dim3((unsigned)nwg), dim3(kPPThreads), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (void*)po, pl, plb,
-                       a.n_q, a.n_k, a.coff, n_qtiles, a.scale * kLog2e, sp.nsplit, sp.kchunk);
+                       a.n_q, a.n_k, a.coff, n_qtiles, a.scale * kLog2e, sp.nsplit, sp.chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_merge_kernel<D, OF32>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
@@ -575,7 +575,7 @@ hipError_t dispatch_pp(const FwdArgs& a, hipStream_t st) {
 }
 
 template <int D>
-hipError_t dispatch_pp_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st) {
+hipError_t dispatch_pp_split(const FwdArgs& a, const Split& sp, float* ws, hipStream_t st) {
     if (a.causal)
         return a.o_f32 ? launch_pp_split<D, true, true>(a, sp, ws, st)
                        : launch_pp_split<D, true, false>(a, sp, ws, st);
@@ -613,43 +613,25 @@ hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t st) {
     }
 }
 
-// Key split for grids that leave most CUs idle: when the 256-row
-// workgroups would occupy at most half of the CUs and there are at least
-// 2048 keys, split each query tile's keys into the fewest chunks (whole
-// 64-key tiles, at least 256 keys each) whose workgroups fill the CUs in
-// whole rounds (or four or more); failing that, into as many as fill one
-// round. Measured: one head of 4096 (16 workgroups) 1.8x faster split; the
+// Key split for grids that leave most CUs idle (one 256-row workgroup per
+// CU; chunks of whole 64-key tiles), by the shared rule of plan_split.
+// Measured: one head of 4096 (16 workgroups) 1.8x faster split; the
 // cross-attention workload (384 workgroups, 3000 keys) 1.5x slower split in
 // two, and one head of 1024 keys slower too (the merge and the partials
 // cost more than the idle CUs): those stay unsplit. Head dims 64 and 128
-// only; nsplit = 1 means no split.
-FwdSplit fwd_split_plan(const FwdArgs& a) {
-    FwdSplit sp{1, a.n_k};
-    if ((a.d != 128 && a.d != 64) || a.n_k < 2048) return sp;
-    const long long nwg = (long long)a.bh * ((a.n_q + kPPRows - 1) / kPPRows);
-    const int cus = device_cu_count();
-    if (cus <= 0 || 2 * nwg > cus) return sp;
-    const int s_max = a.n_k / 256;
-    auto plan = [&](int s) {
-        const int chunk = ((a.n_k + s - 1) / s + kPPBC - 1) / kPPBC * kPPBC;
-        return FwdSplit{(a.n_k + chunk - 1) / chunk, chunk};
-    };
-    for (int s = 2; s <= s_max && nwg * s <= 8LL * cus; ++s) {
-        const FwdSplit p = plan(s);
-        if (fills_cus(nwg * p.nsplit)) return p;
-    }
-    const long long s_round = (cus + nwg - 1) / nwg;   // one full round
-    const int s = (int)(s_round < s_max ? s_round : s_max);
-    return s >= 2 ? plan(s) : sp;
+// only.
+Split fwd_split_plan(const FwdArgs& a) {
+    if (a.d != 128 && a.d != 64) return Split{1, a.n_k};
+    return plan_split((long long)a.bh * ((a.n_q + kPPRows - 1) / kPPRows), device_cu_count(), a.n_k, kPPBC);
 }
 
-size_t fwd_split_workspace_bytes(const FwdArgs& a, const FwdSplit& sp) {
+size_t fwd_split_workspace_bytes(const FwdArgs& a, const Split& sp) {
     if (sp.nsplit <= 1) return 0;
     const size_t rows = (size_t)a.bh * (size_t)a.n_q * (size_t)sp.nsplit;
     return rows * ((size_t)a.d + 2) * sizeof(float);
 }
 
-hipError_t launch_fwd_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st) {
+hipError_t launch_fwd_split(const FwdArgs& a, const Split& sp, float* ws, hipStream_t st) {
     switch (a.d) {
         case 64: return dispatch_pp_split<64>(a, sp, ws, st);
         case 128: return dispatch_pp_split<128>(a, sp, ws, st);

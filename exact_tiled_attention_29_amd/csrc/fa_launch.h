@@ -42,24 +42,50 @@ struct BwdArgs {
     hipEvent_t const* events;  // NULL or 4 events: before D, before dK/dV, after dK/dV, end
     float* dq_part;  // NULL, or fp32 [bh * dq_nsplit, n_q, d]: key-split partials of dQ (bf16 path)
     int dq_nsplit;   // key chunks of the dQ kernel when dq_part is set
-    int dq_kchunk;   // keys per chunk, a multiple of 64
+    int dq_chunk;    // keys per chunk, a multiple of 64
     float* kv_part;  // NULL, or fp32 partials of dK then dV, each [bh * kv_nsplit, n_k, d] (bf16 path)
     int kv_nsplit;   // query chunks of the dK/dV kernel when kv_part is set
-    int kv_qchunk;   // queries per chunk, a multiple of 256
+    int kv_chunk;    // queries per chunk, a multiple of 256
 };
 
-// Key split of the bf16 dQ kernel for grids with few query tiles
-// (fa_bwd.hip); nsplit = 1 means none.
-struct DqSplit {
+// A split of one dimension (keys or queries) of a kernel's work into nsplit
+// chunks of `chunk` rows each (the last one shorter); nsplit = 1: none.
+struct Split {
     int nsplit;
-    int kchunk;
+    int chunk;
 };
-DqSplit dq_split_plan(long long bh, int n_q, int n_k, int d);
-size_t dq_part_bytes(const DqSplit& sp, long long bh, int n_q, int d);
-// Query split of the bf16 dK/dV kernel for grids with few key blocks
-// (nsplit chunks of kchunk = a multiple of 256 queries); nsplit = 1: none.
-DqSplit kv_split_plan(long long bh, int n_q, int n_k, int d);
-size_t kv_part_bytes(const DqSplit& sp, long long bh, int n_k, int d);
+
+// The split rule shared by the forward, dQ and dK/dV kernels. A grid of nwg
+// workgroups over `slots` resident workgroup slots is split only when it
+// would fill at most half of them and the split dimension has n >= 2048
+// rows; then into the fewest chunks (multiples of `unit` rows, at least
+// 256) whose nwg * nsplit workgroups fill the slots in whole rounds or in
+// four or more rounds; failing that, into as many as fill one round.
+inline Split plan_split(long long nwg, long long slots, int n, int unit) {
+    Split none{1, n};
+    if (n < 2048 || slots <= 0 || 2 * nwg > slots) return none;
+    const int s_max = n / 256;
+    auto plan = [&](int s) {
+        const int chunk = ((n + s - 1) / s + unit - 1) / unit * unit;
+        return Split{(n + chunk - 1) / chunk, chunk};
+    };
+    for (int s = 2; s <= s_max && nwg * s <= 8 * slots; ++s) {
+        const Split p = plan(s);
+        const long long w = nwg * p.nsplit;
+        if (w % slots == 0 || w >= 4 * slots) return p;
+    }
+    const long long s_round = (slots + nwg - 1) / nwg;
+    const int s = (int)(s_round < s_max ? s_round : s_max);
+    return s >= 2 ? plan(s) : none;
+}
+
+// Key split of the bf16 dQ kernel for grids with few query tiles and query
+// split of the bf16 dK/dV kernel for grids with few key blocks (fa_bwd.hip),
+// with the bytes of their fp32 partials.
+Split dq_split_plan(long long bh, int n_q, int n_k, int d);
+size_t dq_part_bytes(const Split& sp, long long bh, int n_q, int d);
+Split kv_split_plan(long long bh, int n_q, int n_k, int d);
+size_t kv_part_bytes(const Split& sp, long long bh, int n_k, int d);
 
 // Record stage event i of a backward call (no-op without events).
 inline hipError_t record_stage(const BwdArgs& a, int i, hipStream_t st) {
@@ -88,14 +114,10 @@ bool fwd_pp_supports(const FwdArgs& a);
 hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t st);
 
 // Key-split forward (fa_fwd_pp.hip): nsplit workgroups per query tile, each
-// over kchunk keys (a multiple of 64), then a merge of their partials.
-struct FwdSplit {
-    int nsplit;
-    int kchunk;
-};
-FwdSplit fwd_split_plan(const FwdArgs& a);
-size_t fwd_split_workspace_bytes(const FwdArgs& a, const FwdSplit& sp);
-hipError_t launch_fwd_split(const FwdArgs& a, const FwdSplit& sp, float* ws, hipStream_t st);
+// over `chunk` keys (a multiple of 64), then a merge of their partials.
+Split fwd_split_plan(const FwdArgs& a);
+size_t fwd_split_workspace_bytes(const FwdArgs& a, const Split& sp);
+hipError_t launch_fwd_split(const FwdArgs& a, const Split& sp, float* ws, hipStream_t st);
 
 // float32 path (fp32 FMA).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
