@@ -20,8 +20,9 @@ Prints one JSON line (the last line of stdout). For the headline workload
     30 event-timed steps after 5 warm-up steps;
   * device: rocminfo's CU count and maximum engine clock;
   * power: socket power and GFX clock sampled with amd-smi while the
-    headline step runs back to back for a few seconds (these kernels run at
-    the chip's power limit, below the 2.4 GHz clock the peak assumes);
+    headline step runs back to back for a few seconds (on N(0,1) bf16 data
+    the matrix cores run at about 1.8-1.9 GHz, below the 2.4 GHz clock the
+    peak assumes);
   * cpu_baseline: the fp64 oracle on whole heads of each workload, on a
     thread pool over (head, row chunk) with one BLAS thread per worker, on
     the host cores this job may use; with the GPU/oracle time ratios.
@@ -926,7 +927,7 @@ def main():
         result["configs"] = configs
 
     # Socket power and clock while the headline step runs back to back: the
-    # chip runs these kernels at its power limit, below its 2.4 GHz peak clock.
+    # matrix cores run below the 2.4 GHz clock the peak assumes on N(0,1) data.
     if not args.no_power:
         pw = sustained_power(pr.step, args.power_seconds)
         if pw and pw.get("gfx_clock_mhz"):
