@@ -195,7 +195,9 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         }
     }
 
-    // dV (wave A) or dK (wave B) accumulators: rows = keys, columns = d.
+    // dV (wave A) or dK (wave B) accumulators, transposed: block db holds
+    // rows = d (32 db ..), columns = the pair's keys, so each lane keeps its
+    // own key's row (4 adjacent columns per 4 elements; see the epilogue).
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
@@ -307,11 +309,11 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // acc[db] += X^T T for a staged Q or dO tile T (rows = keys, columns =
-    // d), X = P or dS as A operands (k = query). The B operands carry queries
-    // 16c + 8*(e/4) + 4g + e%4 in slot (g, e), matching the accumulator order
-    // of P and dS, and are read kLookG products ahead; extra(j) runs after
-    // product j and issues about NV VALU instructions.
+    // acc[db] += T^T X for a staged Q or dO tile T (acc rows = d, columns =
+    // keys), X = P or dS as B operands (k = query). The A operands carry
+    // queries 16c + 8*(e/4) + 4g + e%4 in slot (g, e), matching the
+    // accumulator order of P and dS, and are read kLookG products ahead;
+    // extra(j) runs after product j and issues about NV VALU instructions.
     constexpr int kLookG = 3;
     auto keys_times_tile = [&](const bf16* Tb, const bf16x8* xa, auto&& extra, auto nv) {
         constexpr int NV = decltype(nv)::value;
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             if (j + kLookG < NJ) load(j + kLookG);
-            acc[j % NDB] = mfma32(xa[j / NDB], b[j % (kLookG + 1)], acc[j % NDB]);
+            acc[j % NDB] = mfma32(b[j % (kLookG + 1)], xa[j / NDB], acc[j % NDB]);
             extra(j);
         }
         __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * (kLookG < NJ ? kLookG : NJ), 0);
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
 
     // One step's MFMAs of a wave as a single operand stream: KK products
     // acc1 = T1 kv^T (operands read from tile T1 by rows), then NJ products
-    // acc[db] += X^T T2 (operands read from tile T2 by transpose). Operands
+    // acc[db] += T2^T X (operands read from tile T2 by transpose). Operands
     // are read kLook stream positions ahead, across the change of tile, so
     // the second phase starts with its operands in registers. pre() issues
     // NPRE other LDS reads first; extra1(kk) / extra2(j) run after the MFMAs
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                 extra1(i);
             } else {
                 const int j = i - KK;
-                acc[j % NDB] = mfma32(X[j / NDB], op[i % (kLook + 1)], acc[j % NDB]);
+                acc[j % NDB] = mfma32(op[i % (kLook + 1)], X[j / NDB], acc[j % NDB]);
                 extra2(j);
             }
         }
@@ -561,28 +563,58 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         }
     }
 
-    // Epilogue: wave A stores dV, wave B stores dK = scale * acc; rows =
-    // keys kw0 + acc_row(v, g), column = d. Under the query split: the fp32
-    // partials of virtual head bhv.
+    // Epilogue: wave A stores dV, wave B stores dK = scale * acc. Lane (r, g)
+    // holds the row of key kw0 + r; element 4i + j of block db is column
+    // 32 db + 8i + 4g + j. Under the query split the fp32 partials of virtual
+    // head bhv go out directly, 16 bytes per (db, i). Otherwise each wave
+    // stages its 32 x D bf16 block in the (now idle) ring, rows of D * 2
+    // bytes whose 16-byte chunks are XOR-swizzled by row, and stores whole
+    // rows back with 16-byte stores (16 lanes per 256 bytes of a row).
     const float f = role_a ? 1.0f : scale;
     if (part_k) {
-        float* out = role_a ? part_v : part_k;
+        if (key < n_k) {
+            float* out = (role_a ? part_v : part_k) + ((size_t)bhv * n_k + key) * D + 4 * g;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int kr = kw0 + acc_row(v, g);
-                if (kr < n_k) out[((size_t)bhv * n_k + kr) * D + 32 * db + r] = acc[db][v] * f;
-            }
+                for (int i = 0; i < 4; ++i)
+                    *(float4*)(out + 32 * db + 8 * i) =
+                        make_float4(acc[db][4 * i] * f, acc[db][4 * i + 1] * f, acc[db][4 * i + 2] * f,
+                                    acc[db][4 * i + 3] * f);
+        }
     } else {
-        bf16* out = role_a ? dV : dK;
+        constexpr int CH = D / 8;                   // 16-byte chunks per row
+        constexpr int SWM = ((CH & -CH) < 32 ? (CH & -CH) : 32) - 1;   // swizzle mask (stays in the row)
+        constexpr int SB = 32 * D * 2;              // staging bytes per wave
+        constexpr int WPS = SLOT * 2 / SB;          // waves staged per slot
+        static_assert(3 * WPS >= NW, "the staging blocks fit the ring");
+        __syncthreads();   // every wave is done with the ring
+        // (the lane index passes an empty asm so that none of the address
+        // arithmetic below is hoisted above the loop, where it would hold
+        // registers through it)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int rl = ln & 31, gl = ln >> 5;
+        bf16* sl = wave / WPS == 0 ? Sl0 : (wave / WPS == 1 ? Sl1 : Sl2);
+        char* st = (char*)sl + (wave % WPS) * SB;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int kr = kw0 + acc_row(v, g);
-                if (kr < n_k) out[((size_t)bh * n_k + kr) * D + 32 * db + r] = to_bf16(acc[db][v] * f);
+            for (int i = 0; i < 4; ++i) {
+                bf16x4 pk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pk[j] = to_bf16(acc[db][4 * i + j] * f);
+                const int c = 4 * db + i;           // chunk of columns 8c .. 8c + 7
+                *(bf16x4*)(st + rl * D * 2 + 16 * (c ^ (rl & SWM)) + 8 * gl) = pk;
             }
+        bf16* out = (role_a ? dV : dK) + ((size_t)bh * n_k + kw0) * D;
+#pragma unroll
+        for (int k = 0; k < CH / 2; ++k) {
+            const int p = 64 * k + ln;
+            const int row = p / CH, c = p % CH;
+            const bf16x8 x = *(const bf16x8*)(st + row * D * 2 + 16 * (c ^ (row & SWM)));
+            if (kw0 + row < n_k) *(bf16x8*)(out + (size_t)row * D + 8 * c) = x;
+        }
     }
 }
 
