@@ -39,8 +39,9 @@ FA_CAUSAL_TOP_LEFT = 1       # key j visible to query i iff j <= i
 FA_CAUSAL_BOTTOM_RIGHT = 2   # key j visible to query i iff j <= i + n_k - n_q
 
 _STATUS = {0: "FA_OK", 1: "FA_E_NULLPTR", 2: "FA_E_SHAPE", 3: "FA_E_DTYPE", 4: "FA_E_HEADDIM",
-           5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP", 8: "FA_E_CAUSAL", 9: "FA_E_SCRATCH"}
-_ABI_VERSION = 4
+           5: "FA_E_SCALE", 6: "FA_E_WORKSPACE", 7: "FA_E_HIP", 8: "FA_E_CAUSAL", 9: "FA_E_SCRATCH",
+           10: "FA_E_ALIGN"}
+_ABI_VERSION = 5
 # bytes of the library's static per-GPU scratch behind fa_bwd_noalloc
 FA_BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
 _SIZE_MAX = (1 << 64) - 1

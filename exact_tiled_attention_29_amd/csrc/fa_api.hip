@@ -21,6 +21,10 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// The attention kernels move every tensor in 16-byte pieces (direct
+// global -> LDS copies, vector loads and stores).
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 bool dim_ok(int d, int dtype) {
     if (dtype == FA_BF16) return d == 32 || d == 64 || d == 96 || d == 128 || d == 256;
     if (dtype == FA_F32) return d == 16 || d == 32 || d == 64 || d == 96 || d == 128;
@@ -108,7 +112,7 @@ int causal_offset(int causal, int n_q, int n_k) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 4; }
+int fa_abi_version(void) { return 5; }
 
 const char* fa_status_str(int status) {
     switch (status) {
@@ -122,6 +126,7 @@ const char* fa_status_str(int status) {
         case FA_E_HIP: return "HIP runtime error";
         case FA_E_CAUSAL: return "causal must be 0, 1 or 2";
         case FA_E_SCRATCH: return "problem needs more than the library's static backward scratch";
+        case FA_E_ALIGN: return "tensor pointer not 16-byte aligned";
         default: return "unknown status";
     }
 }
@@ -134,6 +139,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, fl
     if (st != FA_OK) return st;
     if (empty) return FA_OK;
     if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_E_ALIGN;
     fa::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.bh = batch * heads; a.n_q = n_q; a.n_k = n_k; a.d = d;
@@ -162,6 +168,7 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, int o_dtype,
     if (st != FA_OK) return st;
     if (empty) return FA_OK;
     if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_E_ALIGN;
     fa::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.bh = batch * heads; a.n_q = n_q; a.n_k = n_k; a.d = d;
@@ -209,12 +216,15 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, int 
         // No query rows: the gradient of K and V is zero.
         if (bh == 0 || n_k == 0) return FA_OK;
         if (!dk || !dv) return FA_E_NULLPTR;
+        if (!aligned16(dk) || !aligned16(dv)) return FA_E_ALIGN;
         const size_t bytes = (size_t)bh * n_k * d * (dtype == FA_BF16 ? 2 : 4);
         hipError_t e = fa::launch_zero(dk, bytes, s);
         if (e == hipSuccess) e = fa::launch_zero(dv, bytes, s);
         return hip_status(e);
     }
     if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return FA_E_NULLPTR;
+    for (const void* p : {q, k, v, o, d_o, (const void*)dq, (const void*)dk, (const void*)dv})
+        if (!aligned16(p)) return FA_E_ALIGN;
     BwdPlan plan = bwd_plan(bh, n_q, n_k, d, dtype);
     if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.kv = fa::Split{1, n_q};
     if (!fits(workspace_bytes_split(bh, n_q, n_k, d, dtype, plan))) plan.dq = fa::Split{1, n_k};

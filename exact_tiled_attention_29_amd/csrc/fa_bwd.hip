@@ -563,13 +563,11 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
         }
     }
 
-    // Epilogue: wave A stores dV, wave B stores dK = scale * acc. Lane (r, g)
-    // holds the row of key kw0 + r; element 4i + j of block db is column
-    // 32 db + 8i + 4g + j. Under the query split the fp32 partials of virtual
-    // head bhv go out directly, 16 bytes per (db, i). Otherwise each wave
-    // stages its 32 x D bf16 block in the (now idle) ring, rows of D * 2
-    // bytes whose 16-byte chunks are XOR-swizzled by row, and stores whole
-    // rows back with 16-byte stores (16 lanes per 256 bytes of a row).
+    // Epilogue: wave A stores dV, wave B stores dK = scale * acc (lane (r, g)
+    // holds the row of key kw0 + r). Under the query split the fp32 partials
+    // of virtual head bhv go out directly, 16 bytes per (db, i); otherwise
+    // each wave stages its bf16 rows in the (now idle) ring and stores them
+    // whole (store_rows_via_lds).
     const float f = role_a ? 1.0f : scale;
     if (part_k) {
         if (key < n_k) {
@@ -583,38 +581,13 @@ __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_kernel(
                                     acc[db][4 * i + 3] * f);
         }
     } else {
-        constexpr int CH = D / 8;                   // 16-byte chunks per row
-        constexpr int SWM = ((CH & -CH) < 32 ? (CH & -CH) : 32) - 1;   // swizzle mask (stays in the row)
         constexpr int SB = 32 * D * 2;              // staging bytes per wave
         constexpr int WPS = SLOT * 2 / SB;          // waves staged per slot
         static_assert(3 * WPS >= NW, "the staging blocks fit the ring");
-        __syncthreads();   // every wave is done with the ring
-        // (the lane index passes an empty asm so that none of the address
-        // arithmetic below is hoisted above the loop, where it would hold
-        // registers through it)
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int rl = ln & 31, gl = ln >> 5;
+        copies_barrier();   // every wave is done with the ring, no copy in flight
         bf16* sl = wave / WPS == 0 ? Sl0 : (wave / WPS == 1 ? Sl1 : Sl2);
-        char* st = (char*)sl + (wave % WPS) * SB;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bf16x4 pk;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pk[j] = to_bf16(acc[db][4 * i + j] * f);
-                const int c = 4 * db + i;           // chunk of columns 8c .. 8c + 7
-                *(bf16x4*)(st + rl * D * 2 + 16 * (c ^ (rl & SWM)) + 8 * gl) = pk;
-            }
-        bf16* out = (role_a ? dV : dK) + ((size_t)bh * n_k + kw0) * D;
-#pragma unroll
-        for (int k = 0; k < CH / 2; ++k) {
-            const int p = 64 * k + ln;
-            const int row = p / CH, c = p % CH;
-            const bf16x8 x = *(const bf16x8*)(st + row * D * 2 + 16 * (c ^ (row & SWM)));
-            if (kw0 + row < n_k) *(bf16x8*)(out + (size_t)row * D + 8 * c) = x;
-        }
+        store_rows_via_lds<D>((char*)sl + (wave % WPS) * SB, (role_a ? dV : dK) + ((size_t)bh * n_k + kw0) * D,
+                              n_k - kw0, [&](int db, int v) { return acc[db][v] * f; });
     }
 }
 
@@ -643,8 +616,11 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE];
     __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE];
 
+    static_assert(32 * D * 4 <= TILE * 2, "a wave's fp32 rows fit one tile buffer");
+
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
 
     int bhv, rank;   // rank 0 = last query tile: longest causal work first
@@ -821,29 +797,15 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void bwd_dq_kernel(
         copies_barrier();
     }
 
-    if (row < n_q) {
-        if (part) {
-            float* pb = part + ((size_t)bhv * n_q + row) * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *(float4*)(pb + 32 * db + 8 * i + 4 * g) =
-                        make_float4(acc[db][4 * i] * scale, acc[db][4 * i + 1] * scale,
-                                    acc[db][4 * i + 2] * scale, acc[db][4 * i + 3] * scale);
-        } else {
-            const size_t obase = ((size_t)bh * n_q + row) * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bf16x4 pk;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) pk[j] = to_bf16(acc[db][4 * i + j] * scale);
-                    *(bf16x4*)(dQ + obase + 32 * db + 8 * i + 4 * g) = pk;
-                }
-        }
-    }
+    // Epilogue: dQ = scale * acc (lane (r, g) holds the row of query qw + r),
+    // or, under the key split, its fp32 partial at virtual head bhv; each
+    // wave stages its 32 rows in one of the (now idle) tile buffers and
+    // stores them whole (store_rows_via_lds; 32 * D * 4 bytes fit a buffer).
+    copies_barrier();   // every wave is done with the tile buffers
+    char* st = (char*)(wave == 0 ? Ks0 : (wave == 1 ? Ks1 : (wave == 2 ? Vs0 : Vs1)));
+    auto value = [&](int db, int v) { return acc[db][v] * scale; };
+    if (part) store_rows_via_lds<D>(st, part + ((size_t)bhv * n_q + qw) * D, n_q - qw, value);
+    else store_rows_via_lds<D>(st, dQ + ((size_t)bh * n_q + qw) * D, n_q - qw, value);
 }
 
 // A gradient as the sum of its split partials ([bh, nsplit, n, D] fp32), in

@@ -215,4 +215,55 @@ __device__ __forceinline__ void work_item(int bid, int n_bh, int n_tiles, int* b
     }
 }
 
+// Store a wave's block of 32 rows x D columns that it holds as the
+// transposed accumulators of 32x32 MFMAs (lane (r, g) owns row r; element
+// 4i + j of block db is column 32 db + 8i + 4g + j) as whole rows, with
+// 16-byte stores: the values go through the wave's own LDS area `st`
+// (32 * D * sizeof(T) bytes, 16-byte aligned, idle meanwhile; rows of
+// D * sizeof(T) bytes whose 16-byte chunks are XOR-swizzled by row, which
+// spreads the staging writes over the banks and keeps each row's read-back
+// conflict-free), then row p goes to out + p * D for p < nrows. Stored
+// directly, each lane's four adjacent columns would make every store
+// instruction touch 32 rows. value(db, v) is element v of block db.
+template <int D, typename T, typename F>
+__device__ __forceinline__ void store_rows_via_lds(char* st, T* out, int nrows, F&& value) {
+    static_assert(sizeof(T) == 2 || sizeof(T) == 4, "bf16 or fp32 rows");
+    constexpr int E = 16 / sizeof(T);          // elements per 16-byte chunk
+    constexpr int CH = D / E;                  // chunks per row
+    constexpr int LOW = CH & -CH;
+    constexpr int SWM = (LOW < 32 ? LOW : 32) - 1;   // XOR mask: stays in the row
+    constexpr int RB = D * (int)sizeof(T);     // bytes per row
+    static_assert(32 * CH % 64 == 0, "whole 16-byte stores per lane");
+    // The lane index passes an empty asm so that none of the address
+    // arithmetic is hoisted above the caller's main loop, where it would
+    // hold registers through it.
+    int ln = threadIdx.x & 63;
+    asm volatile("" : "+v"(ln));
+    const int r = ln & 31, g = ln >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (sizeof(T) == 2) {
+                bf16x4 pk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pk[j] = (bf16)value(db, 4 * i + j);
+                const int c = 4 * db + i;      // columns 8c .. 8c + 7, half g
+                *(bf16x4*)(st + r * RB + 16 * (c ^ (r & SWM)) + 8 * g) = pk;
+            } else {
+                const int c = 8 * db + 2 * i + g;   // columns 4c .. 4c + 3
+                *(float4*)(st + r * RB + 16 * (c ^ (r & SWM))) =
+                    make_float4(value(db, 4 * i), value(db, 4 * i + 1), value(db, 4 * i + 2),
+                                value(db, 4 * i + 3));
+            }
+        }
+#pragma unroll
+    for (int k = 0; k < 32 * CH / 64; ++k) {
+        const int p = 64 * k + ln;
+        const int row = p / CH, c = p % CH;
+        const uint4 x = *(const uint4*)(st + row * RB + 16 * (c ^ (row & SWM)));
+        if (row < nrows) *(uint4*)(out + (size_t)row * D + E * c) = x;
+    }
+}
+
 }  // namespace fa

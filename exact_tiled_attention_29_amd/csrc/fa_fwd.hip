@@ -57,8 +57,11 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
     __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE];
     __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE];
 
+    static_assert(32 * D * 4 <= TILE * 2, "a wave's fp32 rows fit one tile buffer");
+
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, r = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
 
     int bh, rank;   // rank 0 = last query tile: longest causal work first
@@ -262,29 +265,18 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
     }
 
     // Epilogue: O / l, L = ln 2 * (m + log2 l). A row that saw no key has
-    // l = 0 and m = -inf: O = 0 and L = -inf.
+    // l = 0 and m = -inf: O = 0 and L = -inf. Lane (r, g) holds the row of
+    // query qw + r; each wave stages its 32 rows of O in one of the (now
+    // idle) tile buffers and stores them whole (store_rows_via_lds).
     const float l = halves_sum(l_run), lb = halves_sum(lb_run);
     const int row = qw + r;
-    if (row < n_q) {
-        const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
-        const size_t obase = ((size_t)bh * n_q + row) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * g;
-                const float x0 = o[db][4 * i + 0] * inv, x1 = o[db][4 * i + 1] * inv;
-                const float x2 = o[db][4 * i + 2] * inv, x3 = o[db][4 * i + 3] * inv;
-                if (OF32) {
-                    *(float4*)((float*)Out + obase + d0) = make_float4(x0, x1, x2, x3);
-                } else {
-                    bf16x4 pk;
-                    pk[0] = to_bf16(x0); pk[1] = to_bf16(x1); pk[2] = to_bf16(x2); pk[3] = to_bf16(x3);
-                    *(bf16x4*)((bf16*)Out + obase + d0) = pk;
-                }
-            }
-        if (g == 0) Lse[(size_t)bh * n_q + row] = kLn2 * (m_ref + fast_log2(l));
-    }
+    const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
+    copies_barrier();   // every wave is done with the tile buffers
+    char* st = (char*)(wave == 0 ? Ks0 : (wave == 1 ? Ks1 : (wave == 2 ? Vs0 : Vs1)));
+    auto value = [&](int db, int v) { return o[db][v] * inv; };
+    if (OF32) store_rows_via_lds<D>(st, (float*)Out + ((size_t)bh * n_q + qw) * D, n_q - qw, value);
+    else store_rows_via_lds<D>(st, (bf16*)Out + ((size_t)bh * n_q + qw) * D, n_q - qw, value);
+    if (row < n_q && g == 0) Lse[(size_t)bh * n_q + row] = kLn2 * (m_ref + fast_log2(l));
 }
 
 template <int D, bool CAUSAL, bool OF32>

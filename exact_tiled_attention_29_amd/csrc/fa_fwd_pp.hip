@@ -455,31 +455,25 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(
     }
 
     // Epilogue: O / l, L = ln 2 * (m + log2 l); a row that saw no key gets
-    // O = 0, L = -inf.
+    // O = 0, L = -inf. Lane (r, g) holds the row of query qw + r; each wave
+    // stages its 32 rows of O in one of the eight (now idle) ring stages and
+    // stores them whole (store_rows_via_lds). The barrier also waits for the
+    // zero-filling copies the last step may still have in flight into the
+    // stages.
+    static_assert(32 * D * 4 <= TILE * 2, "a wave's fp32 rows fit one stage");
     const float l = halves_sum(l_run), lb = halves_sum(lb_run);
     const int row = qw + r;
-    if (row < n_q) {
-        const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
-        const size_t obase = ((size_t)bhv * n_q + row) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * g;
-                const float x0 = o[db][4 * i + 0] * inv, x1 = o[db][4 * i + 1] * inv;
-                const float x2 = o[db][4 * i + 2] * inv, x3 = o[db][4 * i + 3] * inv;
-                if (OF32) {
-                    *(float4*)((float*)Out + obase + d0) = make_float4(x0, x1, x2, x3);
-                } else {
-                    bf16x4 pk;
-                    pk[0] = to_bf16(x0); pk[1] = to_bf16(x1); pk[2] = to_bf16(x2); pk[3] = to_bf16(x3);
-                    *(bf16x4*)((bf16*)Out + obase + d0) = pk;
-                }
-            }
-        if (g == 0) {
-            Lse[(size_t)bhv * n_q + row] = kLn2 * (m_ref + fast_log2(l));
-            if (Lb) Lb[(size_t)bhv * n_q + row] = kLn2 * (m_ref + fast_log2(lb));
-        }
+    const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
+    copies_barrier();
+    bf16* stg = wave < 4 ? (wave < 2 ? (wave == 0 ? Ks0 : Ks1) : (wave == 2 ? Ks2 : Ks3))
+                         : (wave < 6 ? (wave == 4 ? Vs0 : Vs1) : (wave == 6 ? Vs2 : Vs3));
+    char* st = (char*)stg;
+    auto value = [&](int db, int v) { return o[db][v] * inv; };
+    if (OF32) store_rows_via_lds<D>(st, (float*)Out + ((size_t)bhv * n_q + qw) * D, n_q - qw, value);
+    else store_rows_via_lds<D>(st, (bf16*)Out + ((size_t)bhv * n_q + qw) * D, n_q - qw, value);
+    if (row < n_q && g == 0) {
+        Lse[(size_t)bhv * n_q + row] = kLn2 * (m_ref + fast_log2(l));
+        if (Lb) Lb[(size_t)bhv * n_q + row] = kLn2 * (m_ref + fast_log2(lb));
     }
 }
 

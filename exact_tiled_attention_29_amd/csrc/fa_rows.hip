@@ -11,7 +11,8 @@
 // are all -inf gets L = -inf and a zero softmax row.
 //
 // Rows are read with 16-byte vector loads when every row starts 16-byte
-// aligned (cols a multiple of 16 / sizeof(T)), otherwise element by element.
+// aligned (cols a multiple of 16 / sizeof(T), x and y 16-byte aligned),
+// otherwise element by element.
 // A row of at most 64 lanes x kHold vectors (4096 bf16 or 2048 fp32
 // elements) is held in registers between the two passes, so the softmax
 // reads it from HBM once; longer rows stream twice, four loads in flight per
@@ -180,7 +181,10 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t st) {
     if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
     constexpr int V = Vec16<T>::N;
     const float cs = a.scale * kLog2e;
-    if (a.cols % V != 0)
+    // Vector loads and stores need every row 16-byte aligned: cols a multiple
+    // of the vector and both buffers starting 16-byte aligned.
+    const bool aligned = a.cols % V == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.y & 15) == 0;
+    if (!aligned)
         hipLaunchKernelGGL((row_softmax_kernel<T, YT, 0>), dim3((unsigned)nb), dim3(kRowThreads), 0, st,
                            (const T*)a.x, a.rows, a.cols, cs, a.lse, (YT*)a.y);
     else if (a.cols <= 64 * V * kHold)

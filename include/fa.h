@@ -10,6 +10,8 @@
  *
  * Layout: Q, O, dO, dQ are [batch, heads, n_q, d]; K, V, dK, dV are
  * [batch, heads, n_k, d]; L is [batch, heads, n_q]. Offsets are 64-bit.
+ * Q, K, V, O, dO, dQ, dK and dV must start 16-byte aligned (the kernels
+ * move them in 16-byte pieces), else FA_E_ALIGN.
  *
  * Errors: every argument is checked on the host before any HIP call. On a
  * failed check nothing is launched, no output is touched and a status code
@@ -47,8 +49,9 @@ typedef enum {
     FA_E_WORKSPACE = 6, /* backward workspace NULL or smaller than required    */
     FA_E_HIP = 7,       /* a HIP launch or runtime call failed                 */
     FA_E_CAUSAL = 8,    /* causal is not one of the fa_mask values             */
-    FA_E_SCRATCH = 9    /* fa_bwd_noalloc: the problem needs more scratch than
+    FA_E_SCRATCH = 9,   /* fa_bwd_noalloc: the problem needs more scratch than
                            FA_BWD_NOALLOC_SCRATCH_BYTES                        */
+    FA_E_ALIGN = 10     /* a tensor pointer is not 16-byte aligned             */
 } fa_status;
 
 /* The `causal` argument of fa_fwd / fa_bwd. */
@@ -250,10 +253,11 @@ int fa_row_softmax(const void* x, int dtype, long long rows, int cols, float sca
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 
-/* ABI version of this header: 4 (2 added FA_CAUSAL_BOTTOM_RIGHT and
+/* ABI version of this header: 5 (2 added FA_CAUSAL_BOTTOM_RIGHT and
    FA_E_CAUSAL; 3 added fa_bwd_noalloc and FA_E_SCRATCH, and
    fa_bwd_workspace_bytes returns SIZE_MAX instead of 0 for rejected
-   arguments; 4 added fa_fwd_workspace_bytes and fa_fwd_ws). */
+   arguments; 4 added fa_fwd_workspace_bytes and fa_fwd_ws; 5 added the
+   16-byte alignment check of the tensor pointers and FA_E_ALIGN). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -17,7 +17,7 @@ import exact_tiled_attention_29_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULLPTR, SHAPE, DTYPE, HEADDIM, SCALE, WORKSPACE, HIP, CAUSAL, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
+OK, NULLPTR, SHAPE, DTYPE, HEADDIM, SCALE, WORKSPACE, HIP, CAUSAL, SCRATCH, ALIGN = range(11)
 BF16, F32 = 0, 1
 REJECTED = (1 << 64) - 1   # fa_bwd_workspace_bytes for arguments fa_bwd rejects (SIZE_MAX)
 P = 0x1000  # a non-null dummy pointer; never dereferenced on the validation paths
@@ -52,8 +52,8 @@ def test_library_exports_every_header_function(lib):
 
 
 def test_status_strings(lib):
-    assert lib.fa_abi_version() == 4
-    for code in range(10):
+    assert lib.fa_abi_version() == 5
+    for code in range(11):
         s = fa.fa_status_str(code)
         assert s and s != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
@@ -115,6 +115,25 @@ def test_validation_codes(lib, call):
     assert call(n_k=1 << 23, d=128) == SHAPE
     assert call(n_k=(1 << 23) - 1, d=128, q=None) == NULLPTR
     assert call(dtype=F32, o_dtype=F32, n_k=1 << 22, d=128) == SHAPE
+
+
+@pytest.mark.parametrize("call", [fwd, fwd_ws, bwd])
+def test_tensor_pointers_must_be_16_byte_aligned(lib, call):
+    names = ["q", "k", "v", "o"] + (["d_o", "dq", "dk", "dv"] if call is bwd else [])
+    for name in names:
+        for off in (2, 4, 8):
+            assert call(**{name: P + off}) == ALIGN, (name, off)
+        assert call(**{name: P + 16}) != ALIGN, name
+    # null pointers are reported first; L (fp32, read and written per row)
+    # needs only its natural alignment
+    assert call(q=P + 2, k=None) == NULLPTR
+    assert call(lse=P + 4) != ALIGN
+    # an empty backward still writes dK, dV: they are checked too
+    if call is bwd:
+        assert call(n_q=0, dk=P + 8) == ALIGN
+        assert call(n_q=0, q=P + 8) != ALIGN
+    for name in ("q", "dq", "dv"):
+        assert noalloc(**{name: P + 2}) == ALIGN, name
 
 
 def test_backward_specific_codes(lib):

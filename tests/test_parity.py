@@ -580,6 +580,18 @@ def test_binding_rejects_bad_buffers():
         fa.backward(qg, kg, vg, o, l, dog, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     with pytest.raises(ValueError):
         fa.forward(qg, kg.cpu(), vg, False)
+    # a contiguous view that starts 2 bytes into its storage: refused by the
+    # library's alignment check (FA_E_ALIGN), nothing launched
+    flat = torch.empty(kg.numel() + 8, dtype=kg.dtype, device="cuda")
+    k_odd = flat[1:1 + kg.numel()].view(kg.shape)
+    k_odd.copy_(kg)
+    assert k_odd.is_contiguous() and k_odd.data_ptr() % 16 == 2
+    with pytest.raises(fa.FAError) as err:
+        fa.forward(qg, k_odd, vg, False)
+    assert err.value.status == 10
+    with pytest.raises(fa.FAError) as err:
+        fa.backward(qg, kg, vg, o, l, dog, grads=(dq, dk, flat[1:1 + dv.numel()].view(dv.shape)))
+    assert err.value.status == 10
     # the buffers are usable afterwards
     fa.backward(qg, kg, vg, o, l, dog, grads=(dq, dk, dv))
     torch.cuda.synchronize()
