@@ -233,6 +233,7 @@ __device__ __forceinline__ void store_rows_via_lds(char* st, T* out, int nrows, 
     constexpr int LOW = CH & -CH;
     constexpr int SWM = (LOW < 32 ? LOW : 32) - 1;   // XOR mask: stays in the row
     constexpr int RB = D * (int)sizeof(T);     // bytes per row
+    constexpr int NK = 32 * CH / 64;           // 16-byte stores per lane
     static_assert(32 * CH % 64 == 0, "whole 16-byte stores per lane");
     // The lane index passes an empty asm so that none of the address
     // arithmetic is hoisted above the caller's main loop, where it would
@@ -240,6 +241,7 @@ __device__ __forceinline__ void store_rows_via_lds(char* st, T* out, int nrows, 
     int ln = threadIdx.x & 63;
     asm volatile("" : "+v"(ln));
     const int r = ln & 31, g = ln >> 5;
+    const int rs = r & SWM;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -249,20 +251,46 @@ __device__ __forceinline__ void store_rows_via_lds(char* st, T* out, int nrows, 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) pk[j] = (bf16)value(db, 4 * i + j);
                 const int c = 4 * db + i;      // columns 8c .. 8c + 7, half g
-                *(bf16x4*)(st + r * RB + 16 * (c ^ (r & SWM)) + 8 * g) = pk;
+                *(bf16x4*)(st + r * RB + 16 * (c ^ rs) + 8 * g) = pk;
             } else {
                 const int c = 8 * db + 2 * i + g;   // columns 4c .. 4c + 3
-                *(float4*)(st + r * RB + 16 * (c ^ (r & SWM))) =
+                *(float4*)(st + r * RB + 16 * (c ^ rs)) =
                     make_float4(value(db, 4 * i), value(db, 4 * i + 1), value(db, 4 * i + 2),
                                 value(db, 4 * i + 3));
             }
         }
+    if constexpr (64 % CH == 0) {
+        // Store k covers rows RPI k .. RPI k + RPI - 1 (lane: row RPI k + rb,
+        // chunk c). rb < RPI and RPI is a power of two, so the row's swizzle
+        // bits are rb's plus those of RPI k: the LDS address is one lane
+        // value XOR a constant, plus a constant the read folds into its
+        // offset, and the global address a lane pointer plus a constant.
+        constexpr int RPI = 64 / CH;
+        const int rb = ln / CH, c = ln % CH;
+        const int a0 = rb * RB + 16 * (c ^ (rb & SWM));
+        T* o0 = out + (size_t)rb * D + E * c;
+        auto row_addr = [&](int k) __attribute__((always_inline)) {
+            return st + RPI * k * RB + (a0 ^ (16 * ((RPI * k) & SWM)));
+        };
+        if (nrows >= 32) {
 #pragma unroll
-    for (int k = 0; k < 32 * CH / 64; ++k) {
-        const int p = 64 * k + ln;
-        const int row = p / CH, c = p % CH;
-        const uint4 x = *(const uint4*)(st + row * RB + 16 * (c ^ (row & SWM)));
-        if (row < nrows) *(uint4*)(out + (size_t)row * D + E * c) = x;
+            for (int k = 0; k < NK; ++k)
+                *(uint4*)(o0 + (size_t)RPI * k * D) = *(const uint4*)row_addr(k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+                const uint4 x = *(const uint4*)row_addr(k);
+                if (RPI * k + rb < nrows) *(uint4*)(o0 + (size_t)RPI * k * D) = x;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            const int p = 64 * k + ln;
+            const int row = p / CH, c = p % CH;
+            const uint4 x = *(const uint4*)(st + row * RB + 16 * (c ^ (row & SWM)));
+            if (row < nrows) *(uint4*)(out + (size_t)row * D + E * c) = x;
+        }
     }
 }
 
