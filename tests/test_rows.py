@@ -73,6 +73,28 @@ def test_row_softmax_scale_and_output_dtype(y_dtype):
     _check(x, 2.5, y_dtype, ("scale", y_dtype))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("cols", [512, 4096])
+def test_row_softmax_misaligned_buffers(dtype, cols):
+    # contiguous views that start one element into their storage: the rows
+    # are then not 16-byte aligned, and the kernel must take its element
+    # path (x) / handle the output (y) there too
+    rows = 9
+    x = _inputs(rows, cols, dtype, seed=cols + 1)
+    flat = torch.empty(rows * cols + 8, dtype=dtype, device="cuda")
+    xg = flat[1:1 + rows * cols].view(rows, cols)
+    xg.copy_(x.cuda())
+    assert xg.is_contiguous() and xg.data_ptr() % 16 != 0
+    yflat = torch.empty(rows * cols + 8, dtype=dtype, device="cuda")
+    yg = yflat[1:1 + rows * cols].view(rows, cols)
+    y, lse = fa.row_softmax(xg, 1.0, True, dtype, out=yg)
+    torch.cuda.synchronize()
+    P, L = oracle.row_softmax(x.double().numpy(), 1.0)
+    assert np.abs(lse.cpu().double().numpy() - L).max() <= TOL_L
+    rel = 3e-4 + (2.0 ** -8 if dtype == torch.bfloat16 else 0.0)
+    assert (np.abs(y.cpu().double().numpy() - P) - rel * P).max() <= 1e-7
+
+
 @pytest.mark.parametrize("cols", [40, 512])
 def test_row_softmax_neg_inf_rows_and_entries(cols):
     x = _inputs(6, cols, torch.bfloat16, seed=7)
