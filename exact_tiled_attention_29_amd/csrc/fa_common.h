@@ -114,19 +114,6 @@ __device__ __forceinline__ void copies_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// s_waitcnt immediate for gfx9: vmcnt(vm), expcnt(7), lgkmcnt(lgkm).
-constexpr int waitcnt_imm(int vm, int lgkm) {
-    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
-
-// copies_barrier() that leaves this wave's N most recent copies in flight
-// (a ring that copies two tiles ahead waits only for the older batch).
-template <int N>
-__device__ __forceinline__ void copies_barrier_keep() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 0));
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
 // ds_read_b64_tr_b16: within each 16-lane group, the lane with local index
 // 4*a + e receives element e of the 8-byte chunks addressed by the lanes
 // a, 4 + a, 8 + a, 12 + a (in that order). When lane s of the group points

@@ -48,6 +48,11 @@ constexpr int kPPThreads = 512;
 constexpr int kPPRows = 256;   // query rows per workgroup
 constexpr int kPPBC = 64;      // keys per tile
 
+// s_waitcnt immediate for gfx9: vmcnt(vm), expcnt(7), lgkmcnt(lgkm).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
 // Key split (nsplit > 1): the grid holds nsplit "virtual heads" per head;
 // virtual head bhv = bh * nsplit + s attends head bh's queries to keys
 // [s * kchunk, (s + 1) * kchunk) only and writes its partial result at bhv:
