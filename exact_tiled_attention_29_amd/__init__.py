@@ -100,23 +100,36 @@ def load_library():
 
 # ---- C functions under their own names (pointers as ints) ----
 
+def _i32(**values):
+    """Sizes and codes cross the C ABI as 32-bit ints, which ctypes would
+    wrap without a word (2**32 + 100 arrives as 100): refuse what does not
+    fit."""
+    for name, v in values.items():
+        if not -(1 << 31) <= int(v) < (1 << 31):
+            raise ValueError(f"{name}={v} does not fit the C ABI's 32-bit int")
+
+
 def fa_fwd(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype, causal, scale, stream):
+    _i32(o_dtype=o_dtype, batch=batch, heads=heads, n_q=n_q, n_k=n_k, d=d, dtype=dtype, causal=causal)
     return load_library().fa_fwd(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype,
                                  int(causal), float(scale), stream)
 
 
 def fa_fwd_ws(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype, causal, scale,
               workspace, workspace_bytes, stream):
+    _i32(o_dtype=o_dtype, batch=batch, heads=heads, n_q=n_q, n_k=n_k, d=d, dtype=dtype, causal=causal)
     return load_library().fa_fwd_ws(q, k, v, o, o_dtype, lse, batch, heads, n_q, n_k, d, dtype,
                                     int(causal), float(scale), workspace, workspace_bytes, stream)
 
 
 def fa_fwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, causal):
+    _i32(batch=batch, heads=heads, n_q=n_q, n_k=n_k, d=d, dtype=dtype, causal=causal)
     return load_library().fa_fwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, int(causal))
 
 
 def fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype, causal,
            scale, workspace, workspace_bytes, stream):
+    _i32(o_dtype=o_dtype, batch=batch, heads=heads, n_q=n_q, n_k=n_k, d=d, dtype=dtype, causal=causal)
     return load_library().fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q,
                                  n_k, d, dtype, int(causal), float(scale), workspace,
                                  workspace_bytes, stream)
@@ -124,6 +137,7 @@ def fa_bwd(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d,
 
 def fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype,
                  causal, scale, workspace, workspace_bytes, stream, events):
+    _i32(o_dtype=o_dtype, batch=batch, heads=heads, n_q=n_q, n_k=n_k, d=d, dtype=dtype, causal=causal)
     return load_library().fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads,
                                        n_q, n_k, d, dtype, int(causal), float(scale), workspace,
                                        workspace_bytes, stream, events)
@@ -131,15 +145,18 @@ def fa_bwd_timed(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n
 
 def fa_bwd_noalloc(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads, n_q, n_k, d, dtype,
                    causal, scale, stream):
+    _i32(o_dtype=o_dtype, batch=batch, heads=heads, n_q=n_q, n_k=n_k, d=d, dtype=dtype, causal=causal)
     return load_library().fa_bwd_noalloc(q, k, v, o, o_dtype, lse, d_o, dq, dk, dv, batch, heads,
                                          n_q, n_k, d, dtype, int(causal), float(scale), stream)
 
 
 def fa_row_softmax(x, dtype, rows, cols, scale, lse, y, y_dtype, stream):
+    _i32(dtype=dtype, cols=cols, y_dtype=y_dtype)
     return load_library().fa_row_softmax(x, dtype, rows, cols, float(scale), lse, y, y_dtype, stream)
 
 
 def fa_bwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, causal):
+    _i32(batch=batch, heads=heads, n_q=n_q, n_k=n_k, d=d, dtype=dtype, causal=causal)
     return load_library().fa_bwd_workspace_bytes(batch, heads, n_q, n_k, d, dtype, int(causal))
 
 
@@ -276,7 +293,8 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, grad
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     mask = _mask_code(causal)
-    need = fa_bwd_workspace_bytes(B, H, n_q, n_k, d, dt, mask)
+    with torch.cuda.device(dev):   # the split plan depends on this device's CU count
+        need = fa_bwd_workspace_bytes(B, H, n_q, n_k, d, dt, mask)
     if need == _SIZE_MAX:    # arguments fa_bwd rejects: let it name the error
         need = 0
     if workspace is None:

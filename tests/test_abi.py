@@ -247,6 +247,25 @@ def test_row_softmax_validation_codes(lib):
     assert rows_call(rows=0, cols=0) == OK
 
 
+@pytest.mark.parametrize("call", [fwd, fwd_ws, bwd])
+def test_binding_refuses_sizes_past_32_bits(lib, call):
+    # ctypes would hand 2**32 + 100 to the library as 100: the binding stops
+    # such values before the call (with null pointers, a call that got
+    # through would return NULLPTR instead of raising)
+    for name in ("batch", "heads", "n_q", "n_k", "d"):
+        for bad in ((1 << 32) + 100, 1 << 31, -(1 << 31) - 1):
+            with pytest.raises(ValueError, match=name):
+                call(**{name: bad, "q": None})
+    with pytest.raises(ValueError, match="causal"):
+        call(causal=(1 << 32) + 1, q=None)
+    assert call(n_q=(1 << 31) - 1, q=None) == SHAPE   # fits, and the library refuses it
+    for size_fn in (fa.fa_fwd_workspace_bytes, fa.fa_bwd_workspace_bytes):
+        with pytest.raises(ValueError, match="heads"):
+            size_fn(1, (1 << 32) + 1, 8, 8, 64, BF16, 0)
+    with pytest.raises(ValueError, match="cols"):
+        rows_call(cols=(1 << 32) + 8)
+
+
 def test_python_helpers_refuse_cpu_tensors(lib):
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
