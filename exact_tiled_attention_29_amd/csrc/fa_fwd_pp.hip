@@ -37,6 +37,8 @@
 //    computing its own max; only when that lets a value exceed 2^8 (or on
 //    the first tile) does it compute the true max, rescale O and l and redo
 //    the exponentials. Exact either way: O and l share the reference.
+#include <atomic>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -580,15 +582,20 @@ hipError_t dispatch_pp_split(const FwdArgs& a, const Split& sp, float* ws, hipSt
 }  // namespace
 
 int device_cu_count() {
-    static int cus[64];
+    // zero until first asked for on that device; threads that race on the
+    // first call store the same value
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-            cus[dev] = n;   // every thread that races here writes the same value
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int q = 0;
+        if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && q > 0) {
+            cus[dev].store(q, std::memory_order_relaxed);
+            n = q;
+        }
     }
-    return cus[dev];
+    return n;
 }
 
 // One 256-row workgroup per CU: used when its workgroups fill the CUs in
