@@ -17,8 +17,9 @@
 //     masking); -D is where the dP accumulators of both later kernels start,
 //     so their MFMAs deliver dP - D;
 //  2. bwd_dkdv: key-stationary. One workgroup per 128 keys of one (batch,
-//     head); each of its 4 waves keeps 32 keys' K and V rows in registers as
-//     MFMA operands and their dK, dV in fp32 accumulators, and walks the
+//     head) (64 at d = 256), as 4 wave pairs of 32 keys each: one wave of a
+//     pair keeps the keys' K rows as MFMA operands and their dV in fp32
+//     accumulators, the other their V rows and dK; the workgroup walks the
 //     32-row query tiles (S, dP, dV, dK: 4 products per tile pair);
 //  3. bwd_dq:   query-stationary, shaped like the forward kernel. One
 //     workgroup per 128 queries; each wave keeps 32 queries' Q and dO rows in

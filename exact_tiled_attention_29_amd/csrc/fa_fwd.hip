@@ -22,9 +22,11 @@
 //    O^T += V^T P^T comes from transpose reads of the row-major V tile;
 //  * scores are kept in the exp2 domain (scale * log2 e folded in), the
 //    row max needs one cross-lane step (v_permlane32_swap), l sums the fp32
-//    probabilities and only the PV operand is rounded to bf16 (RNE); O and l
-//    are rescaled only when a row max grows by more than 2^8 (exact: O and l
-//    share the reference max, and O / l does not depend on it);
+//    probabilities (for L) and only the PV operand is rounded to bf16 (RNE);
+//    O is divided by the sum of those bf16 weights, so the rounding of a
+//    dominant weight cancels between O and its divisor; O and both sums are
+//    rescaled only when a row max grows by more than 2^8 (exact: they share
+//    the reference max, and the quotients do not depend on it);
 //  * workgroups are renumbered so each XCD works through whole heads
 //    (K/V reuse in that XCD's L2), longest causal tiles first.
 #include "fa_common.h"
