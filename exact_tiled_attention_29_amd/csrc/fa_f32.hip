@@ -7,7 +7,9 @@
 // or one key row (dK, dV), each lane holding C = D / G of its columns in
 // registers (at most 32: d = 128 is four lanes of 32), and the row's dot
 // products are summed over the group with quad permutes; key/query tiles of
-// 32 rows are staged in LDS and read as broadcasts. The backward's dQ comes from its own pass
+// 32 rows are copied global -> LDS without registers into two buffers (the
+// next tile lands while the current one is used) and read as broadcasts.
+// The backward's dQ comes from its own pass
 // over the key tiles, so no atomics are needed and results are deterministic.
 // The causal diagonal is a runtime offset coff (key j visible to query i iff
 // j <= i + coff); a row that sees no key gets O = 0, L = -inf and zero dQ,
@@ -44,15 +46,20 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
+// Tile of kTile rows from row r0 of a row-major [n, D] fp32 head (one
+// contiguous block) straight into LDS at dst, without registers: the
+// workgroup's waves issue its 1 KB pieces, `wave` taking every NW-th. Rows
+// past n read as zeros through the buffer resource's bound. Byte offsets
+// are unsigned: (n rounded up to the tile) * D * 4 < 2^32.
 template <int D>
-__device__ __forceinline__ void stage_rows(float* dst, const float* src, int row0, int n, int tid) {
-    // kTile x D floats, rows past n are zero.
-    for (int i = tid; i < kTile * D / 4; i += Split<D>::kThreads) {
-        const int row = i / (D / 4), c = i % (D / 4);
-        const int gr = row0 + row;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (gr < n) x = *(const float4*)(src + (size_t)gr * D + 4 * c);
-        *(float4*)(dst + row * D + 4 * c) = x;
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t rs, float* dst, int r0, int wave, int lane) {
+    constexpr int NW = Split<D>::kThreads / 64;   // waves
+    constexpr int NCH = kTile * D * 4 / 1024;      // 1 KB pieces per tile
+    static_assert(NCH % NW == 0, "whole pieces per wave");
+#pragma unroll
+    for (int i = 0; i < NCH / NW; ++i) {
+        const int b = NW * i + wave;
+        load_lds16(rs, ((unsigned)r0 * D + 256u * (unsigned)b + 4u * (unsigned)lane) * 4u, dst + 256 * b);
     }
 }
 
@@ -62,9 +69,14 @@ __global__ __launch_bounds__(Split<D>::kThreads) void fwd_f32_kernel(
     float* __restrict__ O, float* __restrict__ Lse, int n_q, int n_k, int coff, int n_qtiles,
     float scale2) {
     constexpr int G = Split<D>::G, C = Split<D>::C;
-    __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
-    __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
+    // Two buffers per tensor, one LDS object each: tile t + 1 is copied
+    // while tile t is used.
+    __shared__ __attribute__((aligned(16))) float Ks0[kTile * D];
+    __shared__ __attribute__((aligned(16))) float Ks1[kTile * D];
+    __shared__ __attribute__((aligned(16))) float Vs0[kTile * D];
+    __shared__ __attribute__((aligned(16))) float Vs1[kTile * D];
     const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col0 = (tid % G) * C;     // this lane's columns
     const int bh = blockIdx.x / n_qtiles;
     const int q0 = (blockIdx.x % n_qtiles) * kRows;
@@ -81,11 +93,13 @@ __global__ __launch_bounds__(Split<D>::kThreads) void fwd_f32_kernel(
     float m = kNegInf, l = 0.0f;
     int kend = n_k;
     if (CAUSAL) kend = max(0, min(n_k, min(q0 + kRows, n_q) + coff));
-    for (int ks = 0; ks < kend; ks += kTile) {
-        __syncthreads();
-        stage_rows<D>(Ks, Kh, ks, n_k, tid);
-        stage_rows<D>(Vs, Vh, ks, n_k, tid);
-        __syncthreads();
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kh, n_k * D * 4);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vh, n_k * D * 4);
+    auto issue = [&](float* Kd, float* Vd, int ks) __attribute__((always_inline)) {
+        copy_tile<D>(krs, Kd, ks, wave, lane);
+        copy_tile<D>(vrs, Vd, ks, wave, lane);
+    };
+    auto tile = [&](const float* Ks, const float* Vs, int ks) __attribute__((always_inline)) {
         float s[kTile];
         float mx = kNegInf;
 #pragma unroll
@@ -113,6 +127,23 @@ __global__ __launch_bounds__(Split<D>::kThreads) void fwd_f32_kernel(
             for (int c = 0; c < C; ++c) o[c] = fmaf(p, Vs[j * D + col0 + c], o[c]);
         }
         m = m_new;
+    };
+    // Tile t is in buffer t % 2; the barrier after a tile makes the next
+    // one's copies visible and frees the buffer the following copy reuses.
+    const int ntiles = (kend + kTile - 1) / kTile;
+    if (ntiles > 0) {
+        issue(Ks0, Vs0, 0);
+        copies_barrier();
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        // one loop body with the buffers picked at run time: these kernels
+        // wait for all copies at every barrier, so the compiler need not tell
+        // the buffers apart, and a second copy of the body would only hold
+        // more registers
+        const bool odd = t & 1;
+        if (t + 1 < ntiles) issue(odd ? Ks0 : Ks1, odd ? Vs0 : Vs1, (t + 1) * kTile);
+        tile(odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, t * kTile);
+        copies_barrier();
     }
     if (row < n_q) {
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;   // no visible key: O = 0, L = -inf
@@ -149,10 +180,15 @@ __global__ __launch_bounds__(Split<D>::kThreads) void bwd_dkdv_f32_kernel(
     float* __restrict__ dK, float* __restrict__ dV, int n_q, int n_k, int coff, int n_ktiles,
     float scale, float scale2) {
     constexpr int G = Split<D>::G, C = Split<D>::C;
-    __shared__ __attribute__((aligned(16))) float Qs[kTile * D];
-    __shared__ __attribute__((aligned(16))) float dOs[kTile * D];
-    __shared__ float Ls[kTile], Ds[kTile];
+    // Two buffers per tensor (one LDS object each): query tile t + 1 is
+    // copied while tile t is used, with its L2 and D values.
+    __shared__ __attribute__((aligned(16))) float Qs0[kTile * D];
+    __shared__ __attribute__((aligned(16))) float Qs1[kTile * D];
+    __shared__ __attribute__((aligned(16))) float dOs0[kTile * D];
+    __shared__ __attribute__((aligned(16))) float dOs1[kTile * D];
+    __shared__ float Ls0[kTile], Ds0[kTile], Ls1[kTile], Ds1[kTile];
     const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col0 = (tid % G) * C;
     const int bh = blockIdx.x / n_ktiles;
     const int k0 = (blockIdx.x % n_ktiles) * kRows;
@@ -168,17 +204,53 @@ __global__ __launch_bounds__(Split<D>::kThreads) void bwd_dkdv_f32_kernel(
         dk[c] = dv[c] = 0.0f;
     }
     const int qbeg = CAUSAL ? (max(0, k0 - coff) / kTile) * kTile : 0;  // rows >= k0 - coff
-    for (int qs = qbeg; qs < n_q; qs += kTile) {
-        __syncthreads();
-        stage_rows<D>(Qs, Qh, qs, n_q, tid);
-        stage_rows<D>(dOs, dOh, qs, n_q, tid);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, n_q * D * 4);
+    const __amdgpu_buffer_rsrc_t dors = make_rsrc(dOh, n_q * D * 4);
+    auto issue = [&](float* Qd, float* dOd, int qs) __attribute__((always_inline)) {
+        copy_tile<D>(qrs, Qd, qs, wave, lane);
+        copy_tile<D>(dors, dOd, qs, wave, lane);
+    };
+    // L2 (L * log2 e; +inf for a row with no key, so its P is 0) and D of
+    // query tile qs.., one per thread of the first kTile: loaded into
+    // registers when the tile's copy is issued and written to LDS after the
+    // current tile's work, so the loads' latency hides behind it.
+    float l2_next = 0.0f, d_next = 0.0f;
+    auto load_rows = [&](int qs) __attribute__((always_inline)) {
         if (tid < kTile) {
             const int q = qs + tid;
             const float lse = q < n_q ? Lse[(size_t)bh * n_q + q] : kNegInf;
-            Ls[tid] = lse > kNegInf ? lse * kLog2e : __builtin_huge_valf();   // P = 0 if no key
-            Ds[tid] = q < n_q ? drow[(size_t)bh * n_q + q] : 0.0f;
+            l2_next = lse > kNegInf ? lse * kLog2e : __builtin_huge_valf();
+            d_next = q < n_q ? drow[(size_t)bh * n_q + q] : 0.0f;
         }
-        __syncthreads();
+    };
+    auto store_rows = [&](float* Ld, float* Dd) __attribute__((always_inline)) {
+        if (tid < kTile) {
+            Ld[tid] = l2_next;
+            Dd[tid] = d_next;
+        }
+    };
+    // Tile t (rows qbeg + t * kTile ..) is in buffer t % 2; the barrier after
+    // a tile makes the next one visible and frees the buffer the following
+    // copy reuses.
+    const int ntiles = qbeg < n_q ? (n_q - qbeg + kTile - 1) / kTile : 0;
+    if (ntiles > 0) {
+        issue(Qs0, dOs0, qbeg);
+        load_rows(qbeg);
+        store_rows(Ls0, Ds0);
+        copies_barrier();
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        // buffers picked at run time, as in the forward
+        const bool odd = t & 1;
+        const int qs = qbeg + t * kTile;
+        if (t + 1 < ntiles) {
+            issue(odd ? Qs0 : Qs1, odd ? dOs0 : dOs1, qs + kTile);
+            load_rows(qs + kTile);
+        }
+        const float* Qs = odd ? Qs1 : Qs0;
+        const float* dOs = odd ? dOs1 : dOs0;
+        const float* Ls = odd ? Ls1 : Ls0;
+        const float* Ds = odd ? Ds1 : Ds0;
 #pragma unroll 4
         for (int i = 0; i < kTile; ++i) {
             const int q = qs + i;
@@ -199,6 +271,8 @@ __global__ __launch_bounds__(Split<D>::kThreads) void bwd_dkdv_f32_kernel(
                 dk[c] = fmaf(ds, Qs[i * D + col0 + c], dk[c]);
             }
         }
+        if (t + 1 < ntiles) store_rows(odd ? Ls0 : Ls1, odd ? Ds0 : Ds1);
+        copies_barrier();
     }
     if (key < n_k) {
 #pragma unroll
@@ -216,9 +290,14 @@ __global__ __launch_bounds__(Split<D>::kThreads) void bwd_dq_f32_kernel(
     const float* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ drow,
     float* __restrict__ dQ, int n_q, int n_k, int coff, int n_qtiles, float scale, float scale2) {
     constexpr int G = Split<D>::G, C = Split<D>::C;
-    __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
-    __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
+    // Two buffers per tensor (one LDS object each): tile t + 1 is copied
+    // while tile t is used.
+    __shared__ __attribute__((aligned(16))) float Ks0[kTile * D];
+    __shared__ __attribute__((aligned(16))) float Ks1[kTile * D];
+    __shared__ __attribute__((aligned(16))) float Vs0[kTile * D];
+    __shared__ __attribute__((aligned(16))) float Vs1[kTile * D];
     const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col0 = (tid % G) * C;
     const int bh = blockIdx.x / n_qtiles;
     const int q0 = (blockIdx.x % n_qtiles) * kRows;
@@ -238,11 +317,28 @@ __global__ __launch_bounds__(Split<D>::kThreads) void bwd_dq_f32_kernel(
     const float Dr = row < n_q ? drow[(size_t)bh * n_q + row] : 0.0f;
     int kend = n_k;
     if (CAUSAL) kend = max(0, min(n_k, min(q0 + kRows, n_q) + coff));
-    for (int ks = 0; ks < kend; ks += kTile) {
-        __syncthreads();
-        stage_rows<D>(Ks, Kh, ks, n_k, tid);
-        stage_rows<D>(Vs, Vh, ks, n_k, tid);
-        __syncthreads();
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kh, n_k * D * 4);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vh, n_k * D * 4);
+    auto issue = [&](float* Kd, float* Vd, int ks) __attribute__((always_inline)) {
+        copy_tile<D>(krs, Kd, ks, wave, lane);
+        copy_tile<D>(vrs, Vd, ks, wave, lane);
+    };
+    // Tile t is in buffer t % 2, as in the forward.
+    const int ntiles = (kend + kTile - 1) / kTile;
+    if (ntiles > 0) {
+        issue(Ks0, Vs0, 0);
+        copies_barrier();
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        // one loop body with the buffers picked at run time: these kernels
+        // wait for all copies at every barrier, so the compiler need not tell
+        // the buffers apart, and a second copy of the body would only hold
+        // more registers
+        const bool odd = t & 1;
+        if (t + 1 < ntiles) issue(odd ? Ks0 : Ks1, odd ? Vs0 : Vs1, (t + 1) * kTile);
+        const float* Ks = odd ? Ks1 : Ks0;
+        const float* Vs = odd ? Vs1 : Vs0;
+        const int ks = t * kTile;
 #pragma unroll 4
         for (int j = 0; j < kTile; ++j) {
             const int key = ks + j;
@@ -260,6 +356,7 @@ __global__ __launch_bounds__(Split<D>::kThreads) void bwd_dq_f32_kernel(
 #pragma unroll
             for (int c = 0; c < C; ++c) dq[c] = fmaf(ds, Ks[j * D + col0 + c], dq[c]);
         }
+        copies_barrier();
     }
     if (row < n_q) {
         // Ks holds K * 1 (unscaled); q was pre-scaled, so dq needs the scale.
