@@ -400,6 +400,20 @@ def test_edge_shapes_many_heads(B, H, n_q, n_k, d, dtype, causal):
         check_sum_invariants(res, do, dtype, tag)
 
 
+def test_grids_beyond_16_bits():
+    # 66,003 heads of 40 tokens: every kernel's grid (one workgroup per head
+    # here) passes 65,535 workgroups, and the head count is not a multiple
+    # of 8, so the work order takes its non-XCD branch
+    B, H, n, d = 3, 22001, 40, 32
+    w = workloads.custom(B, H, n, n, d, "bf16", True)
+    q, k, v, do = make_inputs(w, seed=7)
+    res = run(q, k, v, do, True)
+    heads = [(0, 0), (1, 11000), (2, 22000)]
+    tag = str((B, H, n, n, d, "bf16", True))
+    check_heads(res, q, k, v, do, True, "bf16", heads, tag=tag)
+    check_sum_invariants(res, do, "bf16", tag)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_page1_backward_demo_shape(causal):
     # Page 1, section 3 demo: n = 70, d = 16, float32 here, loss sum(O^2) so dO = 2 O.
