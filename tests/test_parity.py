@@ -262,6 +262,17 @@ SPLIT_SHAPES = [
 
 @pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", SPLIT_SHAPES)
 def test_split_shapes(B, H, n_q, n_k, d, dtype, causal):
+    _check_split(B, H, n_q, n_k, d, dtype, causal, q_std=1.0)
+
+
+# Peaked scores (q scaled by 8): the chunks' maxima differ by tens of units,
+# so the merge's weights exp(L_s - L) span many orders of magnitude.
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", [SPLIT_SHAPES[1], SPLIT_SHAPES[3], SPLIT_SHAPES[5]])
+def test_split_shapes_peaked(B, H, n_q, n_k, d, dtype, causal):
+    _check_split(B, H, n_q, n_k, d, dtype, causal, q_std=8.0)
+
+
+def _check_split(B, H, n_q, n_k, d, dtype, causal, q_std):
     # the forward and the backward's dQ kernel both split the keys here
     mask = {False: 0, True: 1, "bottom_right": 2}[causal]
     need = fa.fa_fwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask)
@@ -269,11 +280,11 @@ def test_split_shapes(B, H, n_q, n_k, d, dtype, causal):
     base = 2 * ((B * H * ((n_q + 31) // 32 * 32) * 4 + 255) // 256 * 256)
     assert fa.fa_bwd_workspace_bytes(B, H, n_q, n_k, d, fa.FA_BF16, mask) > base, \
         "the backward should hold dQ partials"
-    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal)
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal, q_std=q_std)
     q, k, v, do = make_inputs(w, seed=n_q + 3 * n_k)
     res = run(q, k, v, do, causal)            # forward() splits when asked to
     heads = [(b, h) for b in range(B) for h in range(H)]
-    tag = "split " + str((B, H, n_q, n_k, d, dtype, causal))
+    tag = "split " + str((B, H, n_q, n_k, d, dtype, causal, q_std))
     check_heads(res, q, k, v, do, causal, dtype, heads, tag=tag)
     # the unsplit kernel: the same result up to rounding; the split is
     # deterministic
