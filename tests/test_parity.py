@@ -427,6 +427,24 @@ def test_peaked_scores_in_the_256_row_forward(d, causal):
     check_sum_invariants(res, do, "bf16", tag)
 
 
+@pytest.mark.parametrize("B,H,n_q,n_k,d,dtype,causal", [
+    (1, 2, 300, 400, 32, "bf16", "bottom_right"),
+    (1, 2, 333, 290, 96, "bf16", True),
+    (1, 2, 300, 400, 256, "bf16", False),
+    (1, 2, 257, 300, 64, "f32", True),
+    (1, 2, 100, 190, 128, "f32", "bottom_right"),
+])
+def test_peaked_scores_other_paths(B, H, n_q, n_k, d, dtype, causal):
+    # the same scores spread (q scaled by 8) through the 128-row kernel and
+    # the fp32 kernels, whose rescaling rules differ from the 256-row one
+    w = workloads.custom(B, H, n_q, n_k, d, dtype, causal, q_std=8.0)
+    q, k, v, do = make_inputs(w, seed=n_q + n_k + d)
+    res = run(q, k, v, do, causal)
+    heads = [(0, 0), (0, 1)]
+    tag = str((B, H, n_q, n_k, d, dtype, causal, "q_std=8"))
+    check_heads(res, q, k, v, do, causal, dtype, heads, tag=tag)
+
+
 def test_grids_beyond_16_bits():
     # 66,003 heads of 40 tokens: every kernel's grid (one workgroup per head
     # here) passes 65,535 workgroups, and the head count is not a multiple
