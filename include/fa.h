@@ -5,8 +5,9 @@
  * contiguous row-major array; sizes are plain ints; the stream is a
  * hipStream_t passed as void* (NULL = the default stream). No call allocates
  * or frees device memory. Apart from the static scratch of fa_bwd_noalloc
- * the library keeps no global state, so the other calls may run
- * concurrently on different streams.
+ * the library keeps no global state but a per-device cache of the
+ * compute-unit count (read on first use, safe from any thread), so the other
+ * calls may run concurrently on different streams and host threads.
  *
  * Layout: Q, O, dO, dQ are [batch, heads, n_q, d]; K, V, dK, dV are
  * [batch, heads, n_k, d]; L is [batch, heads, n_q]. Offsets are 64-bit.
